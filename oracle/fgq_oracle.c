@@ -1,0 +1,251 @@
+/*
+ * fgq_oracle.c -- plain, slow, scalar CPU oracle for fine-grained FP8 quantization
+ * and the block-scaled FP8 GEMM.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Nothing on the product path may call this code: only the
+ * tests, the smoke check and the benchmark's CPU-baseline leg use it.  It shares no code,
+ * header, table or constant with the HIP library.
+ *
+ * Method source: the page "Fine-Grained FP8/FP4 Quantization":
+ *   - section "Scaling Granularities": one FP32 scale per 1x128 row tile of an activation
+ *     and one per 128x128 block of a weight;
+ *   - section "DeepGEMM: Tile-wise and Block-wise Scaling": scale tensor shapes
+ *     scale_A [M, K/128] and scale_B [K/128, N/128] (row-major), and the GEMM that, for
+ *     every 128-wide K chunk, multiplies the FP8 partial by scale_A[m,kb]*scale_B[kb,nb]
+ *     and accumulates;
+ *   - table "UE8M0 vs E4M3 Scale Formats": the E4M3 range ends at 448.
+ * Readings where the page is silent (each listed in the design notes):
+ *   - the stored scale is the dequantization scale s = amax / 448 (fp32, IEEE divide);
+ *   - codes are E4M3 of the correctly rounded fp32 quotient x / s, rounded to nearest,
+ *     ties to even, saturating at +-448 (OCP OFP8 "E4M3FN" variant: bias 7, no infinities,
+ *     S.1111.111 is NaN);
+ *   - an all-zero tile gets s = 0 and signed-zero codes;
+ *   - the GEMM reference is dequantize-then-matmul in fp64 and overwrites C.
+ *
+ * Build: gcc -O2 -std=gnu99 -fPIC -shared -ffp-contract=off -fno-fast-math
+ * (no contraction, no fast math: every float operation below is one IEEE binary32 or
+ * binary64 operation with round-to-nearest-even, as written).
+ */
+#include <math.h>
+#include <stdint.h>
+#include <string.h>
+
+/* ------------------------------------------------------------------------------------ */
+/* E4M3 (OCP OFP8 E4M3FN): decode is the closed form of the format definition.          */
+/* ------------------------------------------------------------------------------------ */
+
+/* Value of one E4M3FN code as a double; NaN for S.1111.111. */
+double oracle_e4m3_decode(uint8_t code)
+{
+    int sign = (code >> 7) & 1;
+    int e = (code >> 3) & 0xF;
+    int m = code & 0x7;
+    double mag;
+    if (e == 0xF && m == 0x7)
+        return NAN;
+    if (e == 0)
+        mag = ldexp((double)m / 8.0, -6);            /* subnormal: (m/8) * 2^(1-7) */
+    else
+        mag = ldexp(1.0 + (double)m / 8.0, e - 7);   /* normal: (1+m/8) * 2^(e-7) */
+    return sign ? -mag : mag;
+}
+
+/* The 127 non-negative finite magnitudes, indexed by code 0x00..0x7E (increasing). */
+static double e4m3_mag[127];
+
+/* filled once when the library is loaded, before any thread can call the encoder */
+__attribute__((constructor)) static void e4m3_init(void)
+{
+    for (int c = 0; c < 127; ++c)
+        e4m3_mag[c] = oracle_e4m3_decode((uint8_t)c);
+}
+
+/*
+ * Encode one fp32 value: round to the nearest E4M3FN value, ties to the code whose
+ * mantissa LSB (= code LSB) is 0, saturating at 448.  Written as a nearest-value search
+ * over the sorted table of representable magnitudes.  NaN input is out of contract.
+ */
+uint8_t oracle_e4m3_encode(float y)
+{
+    uint8_t sign = signbit(y) ? 0x80 : 0x00;
+    double a = fabs((double)y);
+    if (a >= 448.0)
+        return (uint8_t)(sign | 0x7E);
+    /* largest code lo with mag[lo] <= a (binary search over the increasing table) */
+    int lo = 0, hi = 126;
+    while (lo < hi) {
+        int mid = (lo + hi + 1) / 2;
+        if (e4m3_mag[mid] <= a)
+            lo = mid;
+        else
+            hi = mid - 1;
+    }
+    if (e4m3_mag[lo] == a)
+        return (uint8_t)(sign | lo);
+    /* a lies strictly between mag[lo] and mag[lo+1]; compare 2a with their sum (exact) */
+    double twice = 2.0 * a;
+    double sum = e4m3_mag[lo] + e4m3_mag[lo + 1];
+    int pick;
+    if (twice < sum)
+        pick = lo;
+    else if (twice > sum)
+        pick = lo + 1;
+    else
+        pick = (lo % 2 == 0) ? lo : lo + 1; /* tie: even mantissa */
+    return (uint8_t)(sign | pick);
+}
+
+/* bf16 bits -> fp32 (exact: the 16 bits are the high half of the binary32 pattern). */
+static float bf16_to_f32(uint16_t h)
+{
+    uint32_t u = (uint32_t)h << 16;
+    float f;
+    memcpy(&f, &u, sizeof f);
+    return f;
+}
+
+/* Quantize one group of n values (given by index list) sharing one scale. */
+static float quantize_group(const uint16_t *x, const int64_t *idx, int64_t n, uint8_t *q)
+{
+    float amax = 0.0f;
+    for (int64_t i = 0; i < n; ++i) {
+        float v = fabsf(bf16_to_f32(x[idx[i]]));
+        if (v > amax)
+            amax = v;
+    }
+    float s = amax / 448.0f;
+    for (int64_t i = 0; i < n; ++i) {
+        float v = bf16_to_f32(x[idx[i]]);
+        if (s == 0.0f)
+            q[idx[i]] = signbit(v) ? 0x80 : 0x00;
+        else
+            q[idx[i]] = oracle_e4m3_encode(v / s);
+    }
+    return s;
+}
+
+/*
+ * Activation quantization, 1x128 tiles along K (rows m0 <= m < m1 only, so callers may
+ * split rows across threads).  X: bf16 bits [M,K] row-major.  Xq: codes [M,K].
+ * sX: fp32 [M, K/128], sX[m*(K/128)+kb] is the scale of X[m, 128kb .. 128kb+127].
+ * Requires K % 128 == 0.  Returns 0, or -1 on a bad shape.
+ */
+int oracle_quantize_act_1x128(const uint16_t *X, uint8_t *Xq, float *sX, int64_t M, int64_t K,
+                              int64_t m0, int64_t m1)
+{
+    if (M < 0 || K < 0 || K % 128 != 0 || m0 < 0 || m1 > M || m0 > m1)
+        return -1;
+    int64_t KB = K / 128;
+    int64_t idx[128];
+    for (int64_t m = m0; m < m1; ++m) {
+        for (int64_t kb = 0; kb < KB; ++kb) {
+            for (int64_t j = 0; j < 128; ++j)
+                idx[j] = m * K + kb * 128 + j;
+            sX[m * KB + kb] = quantize_group(X, idx, 128, Xq);
+        }
+    }
+    return 0;
+}
+
+/*
+ * Weight quantization, 128x128 blocks (block rows kb0 <= kb < kb1 only).
+ * W: bf16 bits [K,N] row-major.  Wq: codes [K,N].  sW: fp32 [K/128, N/128],
+ * sW[kb*(N/128)+nb] is the scale of W[128kb .. 128kb+127][128nb .. 128nb+127].
+ * Requires K % 128 == 0 and N % 128 == 0.  Returns 0, or -1 on a bad shape.
+ */
+int oracle_quantize_weight_128x128(const uint16_t *W, uint8_t *Wq, float *sW, int64_t K,
+                                   int64_t N, int64_t kb0, int64_t kb1)
+{
+    if (K < 0 || N < 0 || K % 128 != 0 || N % 128 != 0 || kb0 < 0 || kb1 > K / 128 || kb0 > kb1)
+        return -1;
+    int64_t NB = N / 128;
+    static __thread int64_t idx[128 * 128];
+    for (int64_t kb = kb0; kb < kb1; ++kb) {
+        for (int64_t nb = 0; nb < NB; ++nb) {
+            int64_t t = 0;
+            for (int64_t r = 0; r < 128; ++r)
+                for (int64_t c = 0; c < 128; ++c)
+                    idx[t++] = (kb * 128 + r) * N + nb * 128 + c;
+            sW[kb * NB + nb] = quantize_group(W, idx, 128 * 128, Wq);
+        }
+    }
+    return 0;
+}
+
+/*
+ * Block-scaled GEMM reference, rows m0 <= m < m1.
+ * a[m,k] = dec(Aq[m,k]) * sA[m, k/128],  b[k,n] = dec(Bq[k,n]) * sB[k/128, n/128]  (fp64)
+ * C[m,n] = sum_k a[m,k] b[k,n]   and   S[m,n] = sum_k |a[m,k] b[k,n]|   (fp64, k ascending).
+ * Aq [M,K], Bq [K,N] row-major codes; C, S [M,N] row-major (S may be NULL).
+ */
+int oracle_gemm_f64(const uint8_t *Aq, const float *sA, const uint8_t *Bq, const float *sB,
+                    int64_t M, int64_t N, int64_t K, double *C, double *S, int64_t m0, int64_t m1)
+{
+    if (M < 0 || N < 0 || K < 0 || K % 128 != 0 || N % 128 != 0 || m0 < 0 || m1 > M || m0 > m1)
+        return -1;
+    int64_t KB = K / 128, NB = N / 128;
+    double dec[256];
+    for (int c = 0; c < 256; ++c)
+        dec[c] = oracle_e4m3_decode((uint8_t)c);
+    for (int64_t m = m0; m < m1; ++m) {
+        double *crow = C + m * N;
+        double *srow = S ? S + m * N : 0;
+        for (int64_t n = 0; n < N; ++n) {
+            crow[n] = 0.0;
+            if (srow)
+                srow[n] = 0.0;
+        }
+        for (int64_t k = 0; k < K; ++k) {
+            double a = dec[Aq[m * K + k]] * (double)sA[m * KB + k / 128];
+            const uint8_t *brow = Bq + k * N;
+            const float *sbrow = sB + (k / 128) * NB;
+            for (int64_t n = 0; n < N; ++n) {
+                double p = a * (dec[brow[n]] * (double)sbrow[n / 128]);
+                crow[n] += p;
+                if (srow)
+                    srow[n] += fabs(p);
+            }
+        }
+    }
+    return 0;
+}
+
+/*
+ * The same reference for an explicit list of output elements (rows[i], cols[i]), each
+ * computed on its own as one dot product over k (ascending) -- for spot checks of
+ * outputs too large to form whole.
+ */
+int oracle_gemm_f64_at(const uint8_t *Aq, const float *sA, const uint8_t *Bq, const float *sB,
+                       int64_t M, int64_t N, int64_t K, const int64_t *rows, const int64_t *cols,
+                       int64_t count, double *C, double *S)
+{
+    if (M < 0 || N < 0 || K < 0 || K % 128 != 0 || N % 128 != 0)
+        return -1;
+    int64_t KB = K / 128, NB = N / 128;
+    double dec[256];
+    for (int c = 0; c < 256; ++c)
+        dec[c] = oracle_e4m3_decode((uint8_t)c);
+    for (int64_t i = 0; i < count; ++i) {
+        int64_t m = rows[i], n = cols[i];
+        if (m < 0 || m >= M || n < 0 || n >= N)
+            return -1;
+        double c = 0.0, s = 0.0;
+        for (int64_t k = 0; k < K; ++k) {
+            double a = dec[Aq[m * K + k]] * (double)sA[m * KB + k / 128];
+            double p = a * (dec[Bq[k * N + n]] * (double)sB[(k / 128) * NB + n / 128]);
+            c += p;
+            s += fabs(p);
+        }
+        C[i] = c;
+        if (S)
+            S[i] = s;
+    }
+    return 0;
+}
+
+/* Element-wise encode of n fp32 values (a loop over oracle_e4m3_encode). */
+void oracle_e4m3_encode_array(const float *y, uint8_t *q, int64_t n)
+{
+    for (int64_t i = 0; i < n; ++i)
+        q[i] = oracle_e4m3_encode(y[i]);
+}
