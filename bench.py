@@ -1,0 +1,224 @@
+"""Benchmark of the fine-grained FP8 hot path on one MI355X.
+
+One step = the whole path on the 4096^3 workload, inputs resident in HBM:
+  1. 1x128 E4M3 quantization of the bf16 activation A [4096,4096]   (fgq_quantize_act_1x128)
+  2. 128x128 E4M3 quantization of the bf16 weight B [4096,4096]      (fgq_quantize_weight_128x128)
+  3. block-scaled FP8 GEMM C = A_q (x) B_q, bf16 C [4096,4096]       (fgq_gemm_fp8_blockscaled)
+value = 2*M*N*K / step time (TFLOP/s of the whole step).  The dominant kernel is the GEMM:
+its roofline entry divides its algorithmic flops by its own average duration (HIP events on
+the stream it runs on) and compares with the dense FP8 MFMA peak.  The standalone
+activation quantizer is measured on X [16384,7168] (rotating buffers so the 256 MB
+Infinity Cache cannot serve the input) against the HBM peak.  The CPU oracle is timed on a
+bounded sample of the same workload (cpu_baseline).
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_FP8_TFLOPS = 5000.0     # MI355X dense FP8 MFMA (no sparsity)
+PEAK_HBM_GBS = 8000.0        # MI355X HBM3E
+METRIC = "block-scaled FP8 GEMM TFLOP/s (% FP8 MFMA peak); quantize GB/s (% HBM)"
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def to_dev_bf16(bits, torch):
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).cuda()
+
+
+def quant_act_bytes(M, K):
+    return 2 * M * K + M * K + 4 * M * (K // 128)
+
+
+def quant_weight_bytes(K, N):
+    return 2 * K * N + K * N + 4 * (K // 128) * (N // 128)
+
+
+def cpu_baseline(A, B):
+    """The oracle as it stands (scalar C, all host threads over independent rows) on the
+    4096^3 workload: quantize A and B, then the fp64 GEMM for all rows."""
+    import oracle
+    nt = oracle.threads()
+    t0 = time.perf_counter()
+    Aq, sA = oracle.quantize_act(A, nt)
+    Bq, sB = oracle.quantize_weight(B, nt)
+    t1 = time.perf_counter()
+    M, K = A.shape
+    N = B.shape[1]
+    oracle.gemm_f64(Aq, sA, Bq, sB, nt)
+    t2 = time.perf_counter()
+    return {
+        "value": 2.0 * M * N * K / (t2 - t1) / 1e12,
+        "unit": "TFLOP/s",
+        "cores": nt,
+        "kind": "oracle",
+        "sample": f"whole 4096^3 step: oracle quantize A and B ({t1 - t0:.2f} s) then fp64 "
+                  f"dequantize-matmul of all {M} rows ({t2 - t1:.2f} s); value = GEMM flops "
+                  f"/ GEMM time",
+        "quantize_GBps": (quant_act_bytes(M, K) + quant_weight_bytes(K, N)) / (t1 - t0) / 1e9,
+        "seconds": t2 - t0,
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--quant-reps", type=int, default=50)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: the path has no multi-GPU stage here "
+              "(run with --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import fine_grained_block_fgq_amd as fgq
+    import synth
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a ROCm GPU", file=sys.stderr)
+        sys.exit(2)
+    fgq.load()
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    # ---- the step workload: 4096^3, A N(0,1), B N(0,0.02), bf16 C -----------------------
+    w = synth.WORKLOADS["sq4096"]
+    M, N, K = w.M, w.N, w.K
+    log(f"generating {w.name} inputs")
+    A_bits, B_bits, _ = synth.workload_inputs("sq4096")
+    A = to_dev_bf16(A_bits, torch)
+    B = to_dev_bf16(B_bits, torch)
+    Aq = torch.empty((M, K), dtype=torch.uint8, device=dev)
+    sA = torch.empty((M, K // 128), dtype=torch.float32, device=dev)
+    Bq = torch.empty((K, N), dtype=torch.uint8, device=dev)
+    sB = torch.empty((K // 128, N // 128), dtype=torch.float32, device=dev)
+    C = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+    stream = torch.cuda.current_stream()
+
+    def step(ev=None):
+        if ev is not None:
+            ev[0].record(stream)
+        fgq.fgq_quantize_act_1x128(A, Aq, sA, stream)
+        if ev is not None:
+            ev[1].record(stream)
+        fgq.fgq_quantize_weight_128x128(B, Bq, sB, stream)
+        if ev is not None:
+            ev[2].record(stream)
+        fgq.fgq_gemm_fp8_blockscaled(Aq, sA, Bq, sB, C, stream=stream)
+        if ev is not None:
+            ev[3].record(stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    # timed region: exactly `steps` steps, no events inside
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms_per_step = (t1 - t0) * 1e3 / args.steps
+
+    # per-kernel durations (HIP events on the launch stream), separate pass
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    for e in evs:
+        step(e)
+    torch.cuda.synchronize()
+    qa_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in evs]))
+    qw_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in evs]))
+    gm_ms = float(np.mean([e[2].elapsed_time(e[3]) for e in evs]))
+    flops = 2.0 * M * N * K
+    gemm_tflops = flops / (gm_ms * 1e-3) / 1e12
+    log(f"step {ms_per_step:.4f} ms | quant A {qa_ms*1e3:.1f} us  quant B {qw_ms*1e3:.1f} us  "
+        f"GEMM {gm_ms*1e3:.1f} us = {gemm_tflops:.0f} TFLOP/s")
+
+    # ---- standalone activation quantizer, X [16384,7168] (rotating buffers) -------------
+    wq = synth.WORKLOADS["actq"]
+    Mq, Kq = wq.M, wq.K
+    X_bits, _, _ = synth.workload_inputs("actq")
+    nbuf = 4
+    Xs = [to_dev_bf16(X_bits, torch) for _ in range(nbuf)]
+    Xqs = [torch.empty((Mq, Kq), dtype=torch.uint8, device=dev) for _ in range(nbuf)]
+    sXs = [torch.empty((Mq, Kq // 128), dtype=torch.float32, device=dev) for _ in range(nbuf)]
+    for i in range(nbuf):
+        fgq.fgq_quantize_act_1x128(Xs[i], Xqs[i], sXs[i], stream)
+    torch.cuda.synchronize()
+    qev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(args.quant_reps)]
+    for r, (e0, e1) in enumerate(qev):
+        i = r % nbuf
+        e0.record(stream)
+        fgq.fgq_quantize_act_1x128(Xs[i], Xqs[i], sXs[i], stream)
+        e1.record(stream)
+    torch.cuda.synchronize()
+    q_ms = float(np.mean([a.elapsed_time(b) for a, b in qev]))
+    q_bytes = quant_act_bytes(Mq, Kq)
+    q_gbs = q_bytes / (q_ms * 1e-3) / 1e9
+    log(f"act quant [16384,7168]: {q_ms*1e3:.1f} us = {q_gbs:.0f} GB/s")
+    del Xs, Xqs, sXs
+
+    out = {
+        "metric": METRIC,
+        "value": round(flops / (ms_per_step * 1e-3) / 1e12, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp8e4m3 x fp8e4m3 -> fp32 (bf16 in/out)",
+        "data": "synthetic (Philox4x32-10 seed 0): A N(0,1), B N(0,0.02)",
+        "config": {"workload": "4096^3 step: quantize A 1x128 + quantize B 128x128 + "
+                               "block-scaled FP8 GEMM, bf16 C",
+                   "M": M, "N": N, "K": K, "out": "bf16"},
+        "roofline": {
+            "bound": "mfma",
+            "kernel": "gemm_fp8_blockscaled_kernel 4096^3 bf16 out",
+            "achieved": round(gemm_tflops, 1),
+            "peak": PEAK_FP8_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": round(gemm_tflops / PEAK_FP8_TFLOPS, 4),
+            "traffic": None,
+        },
+        "kernels_us": {"quantize_act_4096x4096": round(qa_ms * 1e3, 2),
+                       "quantize_weight_4096x4096": round(qw_ms * 1e3, 2),
+                       "gemm_4096^3": round(gm_ms * 1e3, 2)},
+        "quantize": {
+            "workload": "activation quantize X [16384,7168] bf16 -> E4M3 + fp32 [16384,56]",
+            "bound": "hbm",
+            "achieved": round(q_gbs, 1),
+            "peak": PEAK_HBM_GBS,
+            "unit": "GB/s",
+            "frac": round(q_gbs / PEAK_HBM_GBS, 4),
+            "us": round(q_ms * 1e3, 2),
+            "algorithmic_bytes": q_bytes,
+            "traffic": None,
+        },
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        log("timing the CPU oracle on the 4096^3 workload")
+        out["cpu_baseline"] = cpu_baseline(A_bits, B_bits)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,137 @@
+"""Python binding of libfgq, the gfx950 library for fine-grained FP8 quantization and the
+block-scaled FP8 GEMM (page "Fine-Grained FP8/FP4 Quantization").
+
+Argument marshalling only: every step runs in the HIP kernels behind the C ABI declared in
+``include/fgq.h``.  The functions take torch CUDA (ROCm) tensors for device memory and run
+on the current torch stream.  There is no fallback: if ``libfgq.so`` is missing or fails
+to load, every call raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+__all__ = [
+    "FgqError", "library_path", "load", "fgq_quantize_act_1x128",
+    "fgq_quantize_weight_128x128", "fgq_gemm_fp8_blockscaled", "FGQ_OUT_F32", "FGQ_OUT_BF16",
+]
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_HERE, "libfgq.so")
+FGQ_OUT_F32, FGQ_OUT_BF16 = 0, 1
+_lib = None
+
+
+class FgqError(RuntimeError):
+    def __init__(self, fn: str, status: int, message: str):
+        super().__init__(f"{fn} failed: {message} (status {status})")
+        self.status = status
+
+
+def library_path() -> str:
+    return _LIB_PATH
+
+
+def load() -> ctypes.CDLL:
+    """Load libfgq.so (built in-tree by ``__graft_entry__.build()``); raises if absent."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_LIB_PATH):
+        raise FgqError("load", -100, f"{_LIB_PATH} is not built")
+    lib = ctypes.CDLL(_LIB_PATH)
+    p, i64, i32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
+    lib.fgq_quantize_act_1x128.restype = i32
+    lib.fgq_quantize_act_1x128.argtypes = [p, p, p, i64, i64, p]
+    lib.fgq_quantize_weight_128x128.restype = i32
+    lib.fgq_quantize_weight_128x128.argtypes = [p, p, p, i64, i64, p]
+    lib.fgq_gemm_fp8_blockscaled.restype = i32
+    lib.fgq_gemm_fp8_blockscaled.argtypes = [p, p, p, p, p, i64, i64, i64, i32, p]
+    lib.fgq_status_string.restype = ctypes.c_char_p
+    lib.fgq_status_string.argtypes = [i32]
+    lib.fgq_version.restype = i32
+    lib.fgq_version.argtypes = []
+    _lib = lib
+    return lib
+
+
+def _check(fn: str, status: int):
+    if status != 0:
+        raise FgqError(fn, status, load().fgq_status_string(status).decode())
+
+
+def _stream(stream) -> int:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return stream.cuda_stream
+
+
+def _dev(t: torch.Tensor, name: str, dtype, shape):
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise TypeError(f"{name} must be a CUDA (ROCm) tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return t.data_ptr()
+
+
+def _codes_dtype(t: torch.Tensor):
+    return t.dtype if t.dtype in (torch.uint8, torch.float8_e4m3fn) else torch.uint8
+
+
+def fgq_quantize_act_1x128(X: torch.Tensor, Xq: torch.Tensor | None = None,
+                           scale_X: torch.Tensor | None = None, stream=None):
+    """X bf16 [M,K] -> (Xq uint8 E4M3FN codes [M,K], scale_X fp32 [M,K/128])."""
+    lib = load()
+    M, K = X.shape
+    if Xq is None:
+        Xq = torch.empty((M, K), dtype=torch.uint8, device=X.device)
+    if scale_X is None:
+        scale_X = torch.empty((M, K // 128), dtype=torch.float32, device=X.device)
+    _check("fgq_quantize_act_1x128", lib.fgq_quantize_act_1x128(
+        _dev(X, "X", torch.bfloat16, (M, K)), _dev(Xq, "Xq", _codes_dtype(Xq), (M, K)),
+        _dev(scale_X, "scale_X", torch.float32, (M, K // 128)), M, K, _stream(stream)))
+    return Xq, scale_X
+
+
+def fgq_quantize_weight_128x128(W: torch.Tensor, Wq: torch.Tensor | None = None,
+                                scale_W: torch.Tensor | None = None, stream=None):
+    """W bf16 [K,N] -> (Wq uint8 E4M3FN codes [K,N], scale_W fp32 [K/128,N/128])."""
+    lib = load()
+    K, N = W.shape
+    if Wq is None:
+        Wq = torch.empty((K, N), dtype=torch.uint8, device=W.device)
+    if scale_W is None:
+        scale_W = torch.empty((K // 128, N // 128), dtype=torch.float32, device=W.device)
+    _check("fgq_quantize_weight_128x128", lib.fgq_quantize_weight_128x128(
+        _dev(W, "W", torch.bfloat16, (K, N)), _dev(Wq, "Wq", _codes_dtype(Wq), (K, N)),
+        _dev(scale_W, "scale_W", torch.float32, (K // 128, N // 128)), K, N, _stream(stream)))
+    return Wq, scale_W
+
+
+def fgq_gemm_fp8_blockscaled(A_q: torch.Tensor, scale_A: torch.Tensor, B_q: torch.Tensor,
+                             scale_B: torch.Tensor, C: torch.Tensor | None = None,
+                             out_dtype: torch.dtype = torch.bfloat16, stream=None):
+    """C[M,N] = block-scaled A_q[M,K] @ B_q[K,N] (scales [M,K/128] and [K/128,N/128])."""
+    lib = load()
+    M, K = A_q.shape
+    K2, N = B_q.shape
+    if K2 != K:
+        raise ValueError(f"A_q is [{M},{K}] but B_q is [{K2},{N}]")
+    if C is None:
+        C = torch.empty((M, N), dtype=out_dtype, device=A_q.device)
+    code = {torch.float32: FGQ_OUT_F32, torch.bfloat16: FGQ_OUT_BF16}.get(C.dtype)
+    if code is None:
+        raise TypeError(f"C must be float32 or bfloat16, got {C.dtype}")
+    _check("fgq_gemm_fp8_blockscaled", lib.fgq_gemm_fp8_blockscaled(
+        _dev(A_q, "A_q", _codes_dtype(A_q), (M, K)),
+        _dev(scale_A, "scale_A", torch.float32, (M, K // 128)),
+        _dev(B_q, "B_q", _codes_dtype(B_q), (K, N)),
+        _dev(scale_B, "scale_B", torch.float32, (K // 128, N // 128)),
+        _dev(C, "C", C.dtype, (M, N)), M, N, K, code, _stream(stream)))
+    return C

@@ -1,0 +1,111 @@
+// api.cpp -- the C ABI of libfgq (declared in include/fgq.h): argument validation, then
+// the gfx950 launch on the caller's stream.  No allocation, no global mutable state.
+#include "../../include/fgq.h"
+#include "fgq_launch.hpp"
+
+#include <stdint.h>
+
+namespace {
+
+constexpr int64_t kMaxDim = (int64_t(1) << 31) - 1;
+
+bool misaligned(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) != 0; }
+
+// [a, a+na) and [b, b+nb) overlap (byte ranges, empty ranges never overlap)
+bool overlap(const void* a, int64_t na, const void* b, int64_t nb)
+{
+    if (na <= 0 || nb <= 0)
+        return false;
+    const uintptr_t pa = reinterpret_cast<uintptr_t>(a), pb = reinterpret_cast<uintptr_t>(b);
+    return pa < pb + (uintptr_t)nb && pb < pa + (uintptr_t)na;
+}
+
+int launch_status(hipError_t e) { return e == hipSuccess ? FGQ_OK : FGQ_ERR_LAUNCH; }
+
+}  // namespace
+
+extern "C" {
+
+int fgq_version(void) { return 100; }
+
+const char* fgq_status_string(int status)
+{
+    switch (status) {
+    case FGQ_OK: return "ok";
+    case FGQ_ERR_NULL: return "null pointer";
+    case FGQ_ERR_SHAPE: return "invalid shape";
+    case FGQ_ERR_ALIGN: return "pointer not 16-byte aligned";
+    case FGQ_ERR_DTYPE: return "unknown output dtype";
+    case FGQ_ERR_LAUNCH: return "kernel launch failed";
+    case FGQ_ERR_ALIAS: return "output overlaps another buffer";
+    default: return "unknown status";
+    }
+}
+
+int fgq_quantize_act_1x128(const void* X, void* Xq, float* scale_X, int64_t M, int64_t K,
+                           void* stream)
+{
+    if (M < 0 || K < 0 || K % 128 != 0 || M > kMaxDim || K > kMaxDim)
+        return FGQ_ERR_SHAPE;
+    if (M > 0 && K > 0 && M > ((int64_t(1) << 38) / K))
+        return FGQ_ERR_SHAPE;
+    if (M == 0 || K == 0)
+        return FGQ_OK;
+    if (!X || !Xq || !scale_X)
+        return FGQ_ERR_NULL;
+    if (misaligned(X) || misaligned(Xq) || misaligned(scale_X))
+        return FGQ_ERR_ALIGN;
+    const int64_t nx = 2 * M * K, nq = M * K, ns = 4 * M * (K / 128);
+    if (overlap(X, nx, Xq, nq) || overlap(X, nx, scale_X, ns) || overlap(Xq, nq, scale_X, ns))
+        return FGQ_ERR_ALIAS;
+    return launch_status(fgq::launch_quant_act_1x128(X, Xq, scale_X, M, K,
+                                                     static_cast<hipStream_t>(stream)));
+}
+
+int fgq_quantize_weight_128x128(const void* W, void* Wq, float* scale_W, int64_t K,
+                                int64_t N, void* stream)
+{
+    if (K < 0 || N < 0 || K % 128 != 0 || N % 128 != 0 || K / 128 >= 65536 || N > kMaxDim)
+        return FGQ_ERR_SHAPE;
+    if (K == 0 || N == 0)
+        return FGQ_OK;
+    if (!W || !Wq || !scale_W)
+        return FGQ_ERR_NULL;
+    if (misaligned(W) || misaligned(Wq) || misaligned(scale_W))
+        return FGQ_ERR_ALIGN;
+    const int64_t nw = 2 * K * N, nq = K * N, ns = 4 * (K / 128) * (N / 128);
+    if (overlap(W, nw, Wq, nq) || overlap(W, nw, scale_W, ns) || overlap(Wq, nq, scale_W, ns))
+        return FGQ_ERR_ALIAS;
+    return launch_status(fgq::launch_quant_weight_128x128(W, Wq, scale_W, K, N,
+                                                          static_cast<hipStream_t>(stream)));
+}
+
+int fgq_gemm_fp8_blockscaled(const void* A_q, const float* scale_A, const void* B_q,
+                             const float* scale_B, void* C, int64_t M, int64_t N, int64_t K,
+                             int out_dtype, void* stream)
+{
+    if (out_dtype != FGQ_OUT_F32 && out_dtype != FGQ_OUT_BF16)
+        return FGQ_ERR_DTYPE;
+    if (M < 0 || N < 0 || K < 0 || K % 128 != 0 || N % 128 != 0 || M > kMaxDim ||
+        N > kMaxDim || K > kMaxDim)
+        return FGQ_ERR_SHAPE;
+    if (((M + 127) / 128) * (N / 128) > kMaxDim)
+        return FGQ_ERR_SHAPE;
+    if (M == 0 || N == 0)
+        return FGQ_OK;
+    if (!C || (K > 0 && (!A_q || !scale_A || !B_q || !scale_B)))
+        return FGQ_ERR_NULL;
+    if (misaligned(C) || (K > 0 && (misaligned(A_q) || misaligned(scale_A) ||
+                                    misaligned(B_q) || misaligned(scale_B))))
+        return FGQ_ERR_ALIGN;
+    const int64_t nc = M * N * (out_dtype == FGQ_OUT_BF16 ? 2 : 4);
+    if (K > 0 && (overlap(C, nc, A_q, M * K) || overlap(C, nc, B_q, K * N) ||
+                  overlap(C, nc, scale_A, 4 * M * (K / 128)) ||
+                  overlap(C, nc, scale_B, 4 * (K / 128) * (N / 128))))
+        return FGQ_ERR_ALIAS;
+    return launch_status(fgq::launch_gemm_fp8_blockscaled(A_q, scale_A, B_q, scale_B, C, M, N, K,
+                                                          out_dtype == FGQ_OUT_BF16,
+                                                          static_cast<hipStream_t>(stream)));
+}
+
+}  // extern "C"

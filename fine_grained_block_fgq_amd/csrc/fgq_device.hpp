@@ -1,0 +1,119 @@
+// fgq_device.hpp -- gfx950 device helpers shared by the quantization kernels.
+//
+// Quantization rule (page "Fine-Grained FP8/FP4 Quantization", sections "Scaling
+// Granularities" and "DeepGEMM: Tile-wise and Block-wise Scaling"; E4M3 range from its
+// table "UE8M0 vs E4M3 Scale Formats"): a group (1x128 activation tile or 128x128 weight
+// block) shares the fp32 dequantization scale s = amax/448; each element is stored as the
+// E4M3 (OCP E4M3FN) code of the fp32 quotient x/s, rounded to nearest-even.
+//
+// How the device computes it:
+//   * amax is an exact integer max over the bf16 magnitude bits (sign cleared): for
+//     non-NaN values the unsigned order of those bits is the order of |x|;
+//   * s = amax/448 and r = 1/s use IEEE divides once per group and lane;
+//   * per element, y = fl32(x/s) is reached from q = x*r with one exact-remainder
+//     correction (Markstein's quotient correction: e = q*s - x is exact by FMA, then
+//     y = q - e*r).  The negated remainder keeps the sign of zero: -0 stays -0.  Groups
+//     whose s is below 2^-96 (a reciprocal near the fp32 overflow) take a plain divide;
+//   * y is converted by v_cvt_pk_fp8_f32 (gfx950: OCP E4M3FN, nearest-even).  |y| never
+//     exceeds 448*(1+2^-8) < 464, so the convert's overflow-to-NaN never triggers and no
+//     clamp is needed.
+// Every possible (x, amax) pair is run through this path by the device domain-sweep test
+// and compared with the CPU reference bit for bit.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace fgq {
+
+typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+// max over the 8 bf16 magnitudes held in one 16-byte vector, as 16-bit magnitude bits
+__device__ __forceinline__ uint32_t absmax_bits8(u32x4 v)
+{
+    u16x2 a = __builtin_bit_cast(u16x2, v.x & 0x7FFF7FFFu);
+    u16x2 b = __builtin_bit_cast(u16x2, v.y & 0x7FFF7FFFu);
+    u16x2 c = __builtin_bit_cast(u16x2, v.z & 0x7FFF7FFFu);
+    u16x2 d = __builtin_bit_cast(u16x2, v.w & 0x7FFF7FFFu);
+    u16x2 m = __builtin_elementwise_max(__builtin_elementwise_max(a, b),
+                                        __builtin_elementwise_max(c, d));
+    return m.x > m.y ? (uint32_t)m.x : (uint32_t)m.y;
+}
+
+// max across the 16 lanes of a DPP row (row_ror 8, 4, 2, 1): every lane gets the result
+__device__ __forceinline__ uint32_t row16_max(uint32_t v)
+{
+    v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x128, 0xF, 0xF, false));
+    v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x124, 0xF, 0xF, false));
+    v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x122, 0xF, 0xF, false));
+    v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x121, 0xF, 0xF, false));
+    return v;
+}
+
+// max across all 64 lanes (result valid in every lane)
+__device__ __forceinline__ uint32_t wave_max(uint32_t v)
+{
+    v = row16_max(v);
+    uint32_t a = (uint32_t)__builtin_amdgcn_readlane((int)v, 0);
+    uint32_t b = (uint32_t)__builtin_amdgcn_readlane((int)v, 16);
+    uint32_t c = (uint32_t)__builtin_amdgcn_readlane((int)v, 32);
+    uint32_t d = (uint32_t)__builtin_amdgcn_readlane((int)v, 48);
+    return max(max(a, b), max(c, d));
+}
+
+struct GroupScale {
+    float s;    // stored dequantization scale amax/448
+    float r;    // 1/s (0 when s == 0)
+    bool slow;  // s tiny: per-element IEEE divide instead of the reciprocal path
+};
+
+__device__ __forceinline__ GroupScale group_scale(uint32_t amax_bits16)
+{
+    float amax = __uint_as_float(amax_bits16 << 16);
+    GroupScale g;
+    g.s = amax / 448.0f;
+    g.r = (g.s == 0.0f) ? 0.0f : 1.0f / g.s;
+    g.slow = (g.s != 0.0f) && (g.s < 0x1p-96f);
+    return g;
+}
+
+// fl32(x / s) for one element, reciprocal path (groups with s == 0 or s >= 2^-96)
+__device__ __forceinline__ float quotient_fast(float x, const GroupScale& g)
+{
+    float q = x * g.r;
+    float e = __builtin_fmaf(q, g.s, -x);   // exact: q*s - x
+    return __builtin_fmaf(-e, g.r, q);      // q - e*r, rounded once
+}
+
+// quantize 8 bf16 values (one 16-byte vector) to 8 E4M3 codes (one 8-byte vector)
+template <bool SLOW>
+__device__ __forceinline__ u32x2 quantize8_impl(u32x4 v, const GroupScale& g)
+{
+    uint32_t w[4] = {v.x, v.y, v.z, v.w};
+    uint32_t out[2];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+        float x[4] = {__uint_as_float(w[2 * h] << 16), __uint_as_float(w[2 * h] & 0xFFFF0000u),
+                      __uint_as_float(w[2 * h + 1] << 16),
+                      __uint_as_float(w[2 * h + 1] & 0xFFFF0000u)};
+        float y[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            y[i] = SLOW ? x[i] / g.s : quotient_fast(x[i], g);
+        int packed = __builtin_amdgcn_cvt_pk_fp8_f32(y[0], y[1], 0, false);
+        packed = __builtin_amdgcn_cvt_pk_fp8_f32(y[2], y[3], packed, true);
+        out[h] = (uint32_t)packed;
+    }
+    return u32x2{out[0], out[1]};
+}
+
+__device__ __forceinline__ u32x2 quantize8(u32x4 v, const GroupScale& g)
+{
+    u32x2 q = quantize8_impl<false>(v, g);
+    if (__builtin_expect(g.slow, 0))        // divergent only in groups with a tiny scale
+        q = quantize8_impl<true>(v, g);
+    return q;
+}
+
+}  // namespace fgq

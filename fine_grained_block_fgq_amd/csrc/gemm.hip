@@ -1,0 +1,296 @@
+// gemm.hip -- block-scaled FP8 (E4M3) GEMM for gfx950.
+//
+// Page "Fine-Grained FP8/FP4 Quantization", section "DeepGEMM: Tile-wise and Block-wise
+// Scaling": A_q [M,K] with scale_A [M, K/128], B_q [K,N] (N contiguous) with scale_B
+// [K/128, N/128]; for every 128-wide K chunk kb the FP8 partial P = A_q[:,kb] * B_q[kb,:]
+// is multiplied by scale_A[m,kb] * scale_B[kb, n/128] and accumulated in fp32 (the idea of
+// the page's Hopper section: promote each 128-K partial into an fp32 accumulator, here in
+// VGPRs).  C is overwritten, fp32 or bf16.
+//
+// gfx950 mapping:
+//   * one v_mfma_f32_16x16x128_f8f6f4 covers a whole 128-wide K chunk of a 16x16 output
+//     tile, so its result (C-in = 0) IS the chunk partial: the scale is applied by one
+//     v_fma_f32 per output element per chunk, acc = fma(P, sA*sB, acc);
+//   * A/B chunks are staged in LDS, double-buffered, filled by global_load_lds_dwordx4
+//     (direct to LDS, no VGPR staging); 16-byte columns are XOR-swizzled by row so that
+//     fragment reads spread over the banks;
+//   * B stays N-contiguous in LDS; its MFMA operand (one column, 32 consecutive k per lane)
+//     is gathered by ds_read_b64_tr_b8, which transposes an 8(k) x 16(n) byte block across
+//     each 16-lane group;
+//   * scale_A rows of the tile ride along in the LDS stage; scale_B is one scalar per wave
+//     per chunk (a wave's columns never straddle a 128-column block).
+#include "fgq_launch.hpp"
+
+namespace fgq {
+
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+typedef int i32x2 __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+#define LDS __attribute__((address_space(3)))
+
+template <int BM_, int BN_, int WM_, int WN_>
+struct GemmCfg {
+    static constexpr int BM = BM_, BN = BN_, WM = WM_, WN = WN_;
+    static constexpr int NW = WM * WN, NT = 64 * NW;
+    static constexpr int TM = BM / WM, TN = BN / WN;
+    static constexpr int FM = TM / 16, FN = TN / 16;
+    static constexpr int A_BYTES = BM * 128, B_BYTES = 128 * BN, S_BYTES = BM * 4;
+    static constexpr int STAGE = A_BYTES + B_BYTES + S_BYTES;
+    static constexpr int A_LOADS = A_BYTES / 1024;   // 1 KB per wave instruction
+    static constexpr int B_LOADS = B_BYTES / 1024;
+    static constexpr int S_LOADS = BM / 64;           // 256 B per wave instruction
+    static constexpr int B_ROWS_PER_LOAD = 1024 / BN;
+    static constexpr int B_CHUNKS = BN / 16;
+    static_assert(TN <= 128 && 128 % TN == 0, "a wave's columns must sit in one 128-block");
+    static_assert(TM % 16 == 0 && TN % 16 == 0 && BN >= 128 && BM % 64 == 0, "tile shape");
+    static_assert(A_LOADS % NW == 0 && B_LOADS % NW == 0, "loads split evenly over waves");
+    // waits: every wave issues this many direct-to-LDS loads per stage (S loads go to the
+    // first S_LOADS waves); the pipeline waits with the smallest count, which is safe.
+    static constexpr int MIN_LOADS = (A_LOADS + B_LOADS) / NW;
+};
+
+// s_waitcnt vmcnt(N) (gfx9 encoding: vmcnt bits [3:0] and [15:14]; expcnt [6:4] and
+// lgkmcnt [11:8] left at their maxima, i.e. not waited on)
+template <int N>
+__device__ __forceinline__ void wait_vm()
+{
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+}
+
+// workgroup barrier that orders LDS accesses only (no wait on outstanding global loads)
+__device__ __forceinline__ void lds_barrier()
+{
+    // lgkmcnt(0): this wave's LDS reads have returned (vmcnt/expcnt not waited on)
+    __builtin_amdgcn_s_waitcnt(0xC07F);
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+}
+
+// One direct-to-LDS load: 16 bytes per lane from gptr to LDS [lds + 16*lane] (or 4 bytes
+// per lane to [lds + 4*lane]).  Written as inline asm so the compiler's wait-count pass
+// does not see an outstanding LDS write and does not put a vmcnt(0) in front of every LDS
+// read of the other stage; the pipeline waits for these loads explicitly (wait_vm).
+// M0 holds the LDS base; one wait state separates the M0 write from its use.
+__device__ __forceinline__ void dma_b128(const void* gptr, uint32_t lds)
+{
+    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
+                 :
+                 : "v"(gptr), "s"(lds)
+                 : "memory", "m0");
+}
+__device__ __forceinline__ void dma_b32(const void* gptr, uint32_t lds)
+{
+    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dword %0, off"
+                 :
+                 : "v"(gptr), "s"(lds)
+                 : "memory", "m0");
+}
+
+__device__ __forceinline__ uint32_t lds_addr(const uint8_t LDS* p)
+{
+    return (uint32_t)(uintptr_t)p;
+}
+
+template <class Cfg>
+__device__ __forceinline__ void load_stage(uint8_t LDS* stage, const uint8_t* __restrict__ A,
+                                           const float* __restrict__ sA,
+                                           const uint8_t* __restrict__ B, int64_t M,
+                                           int64_t N, int64_t K, int64_t m0, int64_t n0,
+                                           int64_t kb, int wave, int lane)
+{
+    const int64_t KB = K / 128;
+    // A: instruction ia covers tile rows 8ia..8ia+7; lane -> row 8ia + lane/8, physical
+    // 16-byte column lane%8, which holds logical column (lane%8) ^ (row%8).
+#pragma unroll
+    for (int u = 0; u < Cfg::A_LOADS / Cfg::NW; ++u) {
+        const int ia = u * Cfg::NW + wave;
+        const int row = ia * 8 + (lane >> 3);
+        const int c = (lane & 7) ^ (row & 7);
+        int64_t gm = m0 + row;
+        gm = gm < M ? gm : M - 1;
+        dma_b128(A + gm * K + kb * 128 + c * 16, lds_addr(stage + ia * 1024));
+    }
+    // B: instruction ib covers k rows ib*R..ib*R+R-1 (R = 1024/BN); lane -> row
+    // ib*R + lane/(BN/16), physical column lane%(BN/16) holding logical column p ^ (k%8).
+#pragma unroll
+    for (int u = 0; u < Cfg::B_LOADS / Cfg::NW; ++u) {
+        const int ib = u * Cfg::NW + wave;
+        const int k = ib * Cfg::B_ROWS_PER_LOAD + lane / Cfg::B_CHUNKS;
+        const int p = lane % Cfg::B_CHUNKS;
+        const int c = p ^ (k & 7);
+        int64_t gn = n0 + c * 16;
+        gn = gn < N ? gn : N - 16;
+        dma_b128(B + (kb * 128 + k) * N + gn, lds_addr(stage + Cfg::A_BYTES + ib * 1024));
+    }
+    // scale_A rows of the tile: one fp32 per row, gathered with stride K/128.
+    if (wave < Cfg::S_LOADS) {
+        int64_t gm = m0 + wave * 64 + lane;
+        gm = gm < M ? gm : M - 1;
+        dma_b32(sA + gm * KB + kb, lds_addr(stage + Cfg::A_BYTES + Cfg::B_BYTES + wave * 256));
+    }
+}
+
+template <class Cfg, bool OUT_BF16>
+__global__ __launch_bounds__(Cfg::NT) void gemm_fp8_blockscaled_kernel(
+    const uint8_t* __restrict__ A, const float* __restrict__ sA, const uint8_t* __restrict__ B,
+    const float* __restrict__ sB, void* __restrict__ Cout, int64_t M, int64_t N, int64_t K)
+{
+    __shared__ __attribute__((aligned(1024))) uint8_t smem_raw[2 * Cfg::STAGE];
+    uint8_t LDS* const smem = (uint8_t LDS*)smem_raw;
+
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int wm = wave / Cfg::WN, wn = wave % Cfg::WN;
+
+    // tile index: spread consecutive workgroups (which the dispatcher deals round-robin to
+    // the 8 XCDs) so that each XCD works on one contiguous range of tiles, then walk that
+    // range in groups of GROUP_M tile rows so neighbours share A and B panels in L2.
+    const int64_t tiles_m = (M + Cfg::BM - 1) / Cfg::BM;
+    const int64_t tiles_n = (N + Cfg::BN - 1) / Cfg::BN;
+    const int64_t G = (int64_t)gridDim.x;
+    int64_t pid = blockIdx.x;
+    if (G % 8 == 0)
+        pid = (pid % 8) * (G / 8) + pid / 8;
+    constexpr int GROUP_M = 4;
+    const int64_t group = pid / (GROUP_M * tiles_n);
+    const int64_t first_m = group * GROUP_M;
+    const int64_t gsize = (tiles_m - first_m) < GROUP_M ? (tiles_m - first_m) : GROUP_M;
+    const int64_t tm = first_m + (pid % gsize);
+    const int64_t tn = (pid % (GROUP_M * tiles_n)) / gsize;
+    const int64_t m0 = tm * Cfg::BM, n0 = tn * Cfg::BN;
+
+    const int64_t KB = K / 128, NB = N / 128;
+    const int g = lane >> 4;      // k-group of the MFMA operands (32 k each)
+    const int q = lane & 15;      // row (A) / column (B) within a 16x16 fragment
+
+    // per-lane LDS offsets inside a stage
+    int a_off[Cfg::FM][2];
+#pragma unroll
+    for (int i = 0; i < Cfg::FM; ++i) {
+        const int row = wm * Cfg::TM + 16 * i + q;
+        a_off[i][0] = row * 128 + (((2 * g) ^ (row & 7)) * 16);
+        a_off[i][1] = row * 128 + (((2 * g + 1) ^ (row & 7)) * 16);
+    }
+    int b_off[Cfg::FN][4];
+#pragma unroll
+    for (int j = 0; j < Cfg::FN; ++j) {
+        const int ch = (wn * Cfg::TN + 16 * j) / 16;
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+            const int k = 32 * g + 8 * t + (q >> 1);
+            b_off[j][t] = Cfg::A_BYTES + k * Cfg::BN + ((ch ^ (k & 7)) * 16) + 8 * (q & 1);
+        }
+    }
+    const int s_off = Cfg::A_BYTES + Cfg::B_BYTES + (wm * Cfg::TM + 4 * g) * 4;
+    const int64_t nb_wave = (n0 + wn * Cfg::TN) / 128;
+
+    f32x4 acc[Cfg::FM][Cfg::FN];
+#pragma unroll
+    for (int i = 0; i < Cfg::FM; ++i)
+#pragma unroll
+        for (int j = 0; j < Cfg::FN; ++j)
+            acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    if (KB > 0)
+        load_stage<Cfg>(smem, A, sA, B, M, N, K, m0, n0, 0, wave, lane);
+
+    for (int64_t kb = 0; kb < KB; ++kb) {
+        uint8_t LDS* cur = smem + (kb & 1) * Cfg::STAGE;
+        if (kb + 1 < KB) {
+            load_stage<Cfg>(smem + ((kb + 1) & 1) * Cfg::STAGE, A, sA, B, M, N, K, m0, n0,
+                            kb + 1, wave, lane);
+            wait_vm<Cfg::MIN_LOADS>();
+        } else {
+            wait_vm<0>();
+        }
+        lds_barrier();
+
+        // combined scales for this lane's rows: sA[row, kb] * sB[kb, nb]
+        const float sb = (nb_wave < NB) ? sB[kb * NB + nb_wave] : 0.0f;
+        f32x4 cs[Cfg::FM];
+#pragma unroll
+        for (int i = 0; i < Cfg::FM; ++i) {
+            const f32x4 sa = *(const f32x4 LDS*)(cur + s_off + i * 64);
+            cs[i] = sa * sb;
+        }
+        i32x8 af[Cfg::FM];
+#pragma unroll
+        for (int i = 0; i < Cfg::FM; ++i) {
+            const i32x4 lo = *(const i32x4 LDS*)(cur + a_off[i][0]);
+            const i32x4 hi = *(const i32x4 LDS*)(cur + a_off[i][1]);
+            af[i] = i32x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+        }
+#pragma unroll
+        for (int j = 0; j < Cfg::FN; ++j) {
+            i32x2 b0 = __builtin_amdgcn_ds_read_tr8_b64_v2i32((i32x2 LDS*)(cur + b_off[j][0]));
+            i32x2 b1 = __builtin_amdgcn_ds_read_tr8_b64_v2i32((i32x2 LDS*)(cur + b_off[j][1]));
+            i32x2 b2 = __builtin_amdgcn_ds_read_tr8_b64_v2i32((i32x2 LDS*)(cur + b_off[j][2]));
+            i32x2 b3 = __builtin_amdgcn_ds_read_tr8_b64_v2i32((i32x2 LDS*)(cur + b_off[j][3]));
+            const i32x8 bf = i32x8{b0[0], b0[1], b1[0], b1[1], b2[0], b2[1], b3[0], b3[1]};
+#pragma unroll
+            for (int i = 0; i < Cfg::FM; ++i) {
+                const f32x4 p = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+                    af[i], bf, f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0, 0, 0, 0);
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+                    acc[i][j][r] = __builtin_fmaf(p[r], cs[i][r], acc[i][j][r]);
+            }
+        }
+        lds_barrier();
+    }
+
+    // epilogue: lane holds C[16i + 4g + r][16j + q] of the wave tile
+#pragma unroll
+    for (int i = 0; i < Cfg::FM; ++i) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int64_t row = m0 + wm * Cfg::TM + 16 * i + 4 * g + r;
+            if (row >= M)
+                continue;
+#pragma unroll
+            for (int j = 0; j < Cfg::FN; ++j) {
+                const int64_t col = n0 + wn * Cfg::TN + 16 * j + q;
+                if (col >= N)
+                    continue;
+                if (OUT_BF16)
+                    static_cast<__bf16*>(Cout)[row * N + col] = (__bf16)acc[i][j][r];
+                else
+                    static_cast<float*>(Cout)[row * N + col] = acc[i][j][r];
+            }
+        }
+    }
+}
+
+template <class Cfg>
+static hipError_t launch_cfg(const void* A_q, const float* sA, const void* B_q, const float* sB,
+                             void* C, int64_t M, int64_t N, int64_t K, int out_bf16,
+                             hipStream_t stream)
+{
+    const int64_t tiles = ((M + Cfg::BM - 1) / Cfg::BM) * ((N + Cfg::BN - 1) / Cfg::BN);
+    if (out_bf16)
+        hipLaunchKernelGGL((gemm_fp8_blockscaled_kernel<Cfg, true>), dim3((unsigned)tiles),
+                           dim3(Cfg::NT), 0, stream, static_cast<const uint8_t*>(A_q), sA,
+                           static_cast<const uint8_t*>(B_q), sB, C, M, N, K);
+    else
+        hipLaunchKernelGGL((gemm_fp8_blockscaled_kernel<Cfg, false>), dim3((unsigned)tiles),
+                           dim3(Cfg::NT), 0, stream, static_cast<const uint8_t*>(A_q), sA,
+                           static_cast<const uint8_t*>(B_q), sB, C, M, N, K);
+    return hipGetLastError();
+}
+
+using CfgLarge = GemmCfg<256, 256, 4, 2>;
+using CfgSmall = GemmCfg<128, 128, 2, 2>;
+
+hipError_t launch_gemm_fp8_blockscaled(const void* A_q, const float* sA, const void* B_q,
+                                       const float* sB, void* C, int64_t M, int64_t N,
+                                       int64_t K, int out_bf16, hipStream_t stream)
+{
+    if (M >= 256 && N >= 256 && N % 256 == 0)
+        return launch_cfg<CfgLarge>(A_q, sA, B_q, sB, C, M, N, K, out_bf16, stream);
+    return launch_cfg<CfgSmall>(A_q, sA, B_q, sB, C, M, N, K, out_bf16, stream);
+}
+
+}  // namespace fgq

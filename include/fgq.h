@@ -1,0 +1,102 @@
+/*
+ * fgq.h -- C ABI of libfgq: fine-grained FP8 (E4M3) quantization and the block-scaled FP8
+ * GEMM on AMD MI355X (gfx950).
+ *
+ * Method: page "Fine-Grained FP8/FP4 Quantization".
+ *   - section "Scaling Granularities": activations get one fp32 scale per 1x128 row tile,
+ *     weights one per 128x128 block;
+ *   - section "DeepGEMM: Tile-wise and Block-wise Scaling": scale_A is [M, K/128] and
+ *     scale_B is [K/128, N/128], both fp32 row-major; the GEMM multiplies every 128-wide
+ *     K-chunk partial of A_q * B_q by scale_A[m,kb] * scale_B[kb,nb] and accumulates in fp32;
+ *   - table "UE8M0 vs E4M3 Scale Formats": E4M3 reaches 448.
+ * Readings fixed here where the page is silent: the stored scale is s = amax/448 (fp32
+ * IEEE divide) so that x ~= code_value * s; codes are OCP E4M3FN ("fn": bias 7, no
+ * infinities, 0x7F/0xFF NaN) of fl32(x/s), rounded to nearest-even, saturating at 448; an
+ * all-zero group has s = 0 and signed-zero codes; the GEMM overwrites C.
+ *
+ * Conventions for every entry point:
+ *   - All data pointers are DEVICE pointers (HIP/ROCm memory on the current device), owned
+ *     by the caller; the library allocates and frees nothing.  They must be 16-byte
+ *     aligned.  Inputs and outputs must not overlap.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the default stream).  Calls are
+ *     asynchronous on that stream; they return after the launch.
+ *   - The return value reports argument validation and the launch status only
+ *     (FGQ_OK or a negative fgq_status).  On an error nothing is launched and no output is
+ *     touched.  Faults inside a kernel surface on the caller's next synchronisation.
+ *   - Empty problems (a zero dimension) are valid and launch nothing, except that the GEMM
+ *     with K == 0 writes C = 0.
+ *   - No global mutable state: concurrent calls on different streams are safe.
+ */
+#ifndef FGQ_H
+#define FGQ_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    FGQ_OK = 0,
+    FGQ_ERR_NULL = -1,   /* a required pointer is NULL */
+    FGQ_ERR_SHAPE = -2,  /* negative size, K or N not a multiple of 128, or size too large */
+    FGQ_ERR_ALIGN = -3,  /* a pointer is not 16-byte aligned */
+    FGQ_ERR_DTYPE = -4,  /* unknown out_dtype */
+    FGQ_ERR_LAUNCH = -5, /* the HIP launch failed (hipGetLastError) */
+    FGQ_ERR_ALIAS = -6   /* an output overlaps an input or another output */
+} fgq_status;
+
+typedef enum { FGQ_OUT_F32 = 0, FGQ_OUT_BF16 = 1 } fgq_out_dtype;
+
+/*
+ * 1x128 activation quantization.
+ *   X       in : bf16 [M, K] row-major (2*M*K bytes)
+ *   Xq      out: E4M3FN codes [M, K] row-major (M*K bytes)
+ *   scale_X out: fp32 [M, K/128] row-major; scale_X[m*(K/128)+kb] = amax/448 of
+ *                X[m, 128kb .. 128kb+127]
+ * Requires M >= 0, K >= 0, K % 128 == 0, M*K <= 2^38.
+ */
+int fgq_quantize_act_1x128(const void* X, void* Xq, float* scale_X, int64_t M, int64_t K,
+                           void* stream);
+
+/*
+ * 128x128 weight quantization.
+ *   W       in : bf16 [K, N] row-major (N contiguous)
+ *   Wq      out: E4M3FN codes [K, N] row-major
+ *   scale_W out: fp32 [K/128, N/128] row-major; scale_W[kb*(N/128)+nb] = amax/448 of
+ *                W[128kb .. 128kb+127][128nb .. 128nb+127]
+ * Requires K, N >= 0 and multiples of 128, K/128 < 65536, N/128 < 2^31.
+ */
+int fgq_quantize_weight_128x128(const void* W, void* Wq, float* scale_W, int64_t K,
+                                int64_t N, void* stream);
+
+/*
+ * Block-scaled FP8 GEMM:
+ *   C[m,n] = sum_{kb < K/128} scale_A[m,kb] * scale_B[kb, n/128]
+ *                             * sum_{k in chunk kb} dec(A_q[m,k]) * dec(B_q[k,n])
+ * with the chunk partial formed by the FP8 matrix cores and every scaled partial added to
+ * an fp32 accumulator (summation order differs from a serial sum: results are correct to
+ * fp32 rounding, not bit-identical to any particular order).
+ *   A_q     in : E4M3FN [M, K] row-major       scale_A in: fp32 [M, K/128] row-major
+ *   B_q     in : E4M3FN [K, N] row-major (N contiguous)
+ *   scale_B in : fp32 [K/128, N/128] row-major
+ *   C       out: [M, N] row-major, fp32 (out_dtype FGQ_OUT_F32) or bf16 rounded to
+ *                nearest-even (FGQ_OUT_BF16); overwritten.
+ * Requires M, N, K >= 0, K % 128 == 0, N % 128 == 0, every dimension below 2^31 and
+ * ceil(M/128) * (N/128) below 2^31 (the number of output tiles).
+ */
+int fgq_gemm_fp8_blockscaled(const void* A_q, const float* scale_A, const void* B_q,
+                             const float* scale_B, void* C, int64_t M, int64_t N, int64_t K,
+                             int out_dtype, void* stream);
+
+/* Static text for a status code. */
+const char* fgq_status_string(int status);
+
+/* ABI version (major*10000 + minor*100 + patch). */
+int fgq_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FGQ_H */

@@ -1,0 +1,89 @@
+"""The C ABI library loads and exports every entry point include/fgq.h declares; host-side
+argument validation rejects bad calls before any launch (no GPU needed: every call here
+fails validation, so nothing reaches the device)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import fine_grained_block_fgq_amd as fgq
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "fgq.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(fgq_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_library_exports_declared_symbols():
+    lib = fgq.load()
+    names = declared_functions()
+    assert {"fgq_quantize_act_1x128", "fgq_quantize_weight_128x128",
+            "fgq_gemm_fp8_blockscaled"} <= set(names)
+    for n in names:
+        assert hasattr(lib, n), n
+    assert lib.fgq_version() >= 100
+
+
+def test_status_strings():
+    lib = fgq.load()
+    for s in (0, -1, -2, -3, -4, -5, -6):
+        assert lib.fgq_status_string(s)
+    assert lib.fgq_status_string(-99) == b"unknown status"
+
+
+P = 0x10000  # aligned fake addresses: validation fails before they could be used
+Q = 0x20000
+R = 0x30000
+
+
+@pytest.mark.parametrize("args,want", [
+    ((P, Q, R, 4, 100), -2),          # K % 128
+    ((P, Q, R, -1, 128), -2),         # negative M
+    ((P, Q, R, 1 << 31, 128), -2),    # too large
+    ((None, Q, R, 4, 128), -1),       # null
+    ((P + 2, Q, R, 4, 128), -3),      # misaligned
+    ((P, P + 64, R, 4, 128), -6),     # codes overlap X
+    ((P, Q, P + 256, 4, 128), -6),    # scales overlap X
+    ((None, None, None, 0, 128), 0),  # empty: no-op
+    ((None, None, None, 4, 0), 0),
+])
+def test_act_validation(args, want):
+    assert fgq.load().fgq_quantize_act_1x128(*args, None) == want
+
+
+@pytest.mark.parametrize("args,want", [
+    ((P, Q, R, 128, 100), -2),
+    ((P, Q, R, 100, 128), -2),
+    ((P, Q, R, 128 * 65536, 128), -2),
+    ((P, None, R, 128, 128), -1),
+    ((P, Q, R + 4, 128, 128), -3),
+    ((P, P + 16, R, 128, 128), -6),
+    ((None, None, None, 0, 128), 0),
+])
+def test_weight_validation(args, want):
+    assert fgq.load().fgq_quantize_weight_128x128(*args, None) == want
+
+
+S1, S2 = 0x40000, 0x50000
+
+
+@pytest.mark.parametrize("args,want", [
+    ((P, S1, Q, S2, R, 4, 128, 128, 2), -4),      # dtype
+    ((P, S1, Q, S2, R, 4, 100, 128, 0), -2),      # N % 128
+    ((P, S1, Q, S2, R, 4, 128, 100, 0), -2),      # K % 128
+    ((P, S1, Q, S2, R, -4, 128, 128, 0), -2),
+    ((P, None, Q, S2, R, 4, 128, 128, 0), -1),
+    ((P, S1, Q, S2, None, 4, 128, 128, 0), -1),
+    ((P, S1, Q + 8, S2, R, 4, 128, 128, 0), -3),
+    ((P, S1, Q, S2, P, 4, 128, 128, 0), -6),      # C overlaps A_q
+    ((P, S1, Q, S2, S2 - 16, 4, 128, 128, 1), -6),  # C overlaps scale_B
+    ((None, None, None, None, None, 0, 128, 128, 0), 0),
+    ((None, None, None, None, None, 4, 0, 128, 0), 0),
+])
+def test_gemm_validation(args, want):
+    assert fgq.load().fgq_gemm_fp8_blockscaled(*args, None) == want
