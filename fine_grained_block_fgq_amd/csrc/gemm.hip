@@ -8,14 +8,20 @@
 // VGPRs).  C is overwritten, fp32 or bf16.
 //
 // gfx950 mapping:
-//   * one v_mfma_f32_16x16x128_f8f6f4 covers a whole 128-wide K chunk of a 16x16 output
-//     tile, so its result (C-in = 0) IS the chunk partial: the scale is applied by one
-//     v_fma_f32 per output element per chunk, acc = fma(P, sA*sB, acc);
-//   * A/B chunks are staged in LDS, double-buffered, filled by global_load_lds_dwordx4
-//     (direct to LDS, no VGPR staging); 16-byte columns are XOR-swizzled by row so that
-//     fragment reads spread over the banks;
-//   * B stays N-contiguous in LDS; its MFMA operand (one column, 32 consecutive k per lane)
-//     is gathered by ds_read_b64_tr_b8, which transposes an 8(k) x 16(n) byte block across
+//   * the chunk partial is formed by f16 MFMAs (v_mfma_f32_16x16x32_f16, four chained per
+//     128-K chunk) on operands converted exactly from E4M3 (every E4M3 value is an f16
+//     value).  The FP8 MFMAs of gfx950 are not used for the partial: their internal sum
+//     keeps only about 14 bits below the largest product of a reduction, measured at up to
+//     1.9e-4 * sum|a*b| of error per 128-K chunk, while the f16 MFMA sums to fp32 accuracy
+//     (about 3e-7 * sum|a*b|), the accuracy the fp32 accumulation of the method needs;
+//   * the scale is applied by one v_fma_f32 per output element per chunk,
+//     acc = fma(P, sA*sB, acc);
+//   * A/B chunks are staged in LDS as E4M3 bytes, double-buffered, filled by
+//     global_load_lds_dwordx4 (direct to LDS, no VGPR staging); 16-byte columns are
+//     XOR-swizzled by row so that fragment reads spread over the banks; operands are
+//     converted to f16 in registers after the LDS read (v_cvt_scalef32_pk_f16_fp8);
+//   * B stays N-contiguous in LDS; its operand (one column, consecutive k per lane) is
+//     gathered by ds_read_b64_tr_b8, which transposes an 8(k) x 16(n) byte block across
 //     each 16-lane group;
 //   * scale_A rows of the tile ride along in the LDS stage; scale_B is one scalar per wave
 //     per chunk (a wave's columns never straddle a 128-column block).
@@ -27,6 +33,18 @@ typedef int i32x8 __attribute__((ext_vector_type(8)));
 typedef int i32x4 __attribute__((ext_vector_type(4)));
 typedef int i32x2 __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+
+// 8 E4M3 codes (two dwords) -> 8 f16, exact
+__device__ __forceinline__ f16x8 e4m3x8_to_f16(int w0, int w1)
+{
+    const f16x2 a = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w0, 1.0f, false);
+    const f16x2 b = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w0, 1.0f, true);
+    const f16x2 c = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w1, 1.0f, false);
+    const f16x2 d = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w1, 1.0f, true);
+    return f16x8{a[0], a[1], b[0], b[1], c[0], c[1], d[0], d[1]};
+}
 #define LDS __attribute__((address_space(3)))
 
 template <int BM_, int BN_, int WM_, int WN_>
@@ -216,24 +234,33 @@ __global__ __launch_bounds__(Cfg::NT) void gemm_fp8_blockscaled_kernel(
             const f32x4 sa = *(const f32x4 LDS*)(cur + s_off + i * 64);
             cs[i] = sa * sb;
         }
-        i32x8 af[Cfg::FM];
+        // A operands: lane bytes 8s..8s+7 of its 32 (k = 32g + 8s + b) -> sub-step s
+        f16x8 af[Cfg::FM][4];
 #pragma unroll
         for (int i = 0; i < Cfg::FM; ++i) {
             const i32x4 lo = *(const i32x4 LDS*)(cur + a_off[i][0]);
             const i32x4 hi = *(const i32x4 LDS*)(cur + a_off[i][1]);
-            af[i] = i32x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+            af[i][0] = e4m3x8_to_f16(lo[0], lo[1]);
+            af[i][1] = e4m3x8_to_f16(lo[2], lo[3]);
+            af[i][2] = e4m3x8_to_f16(hi[0], hi[1]);
+            af[i][3] = e4m3x8_to_f16(hi[2], hi[3]);
         }
 #pragma unroll
         for (int j = 0; j < Cfg::FN; ++j) {
-            i32x2 b0 = __builtin_amdgcn_ds_read_tr8_b64_v2i32((i32x2 LDS*)(cur + b_off[j][0]));
-            i32x2 b1 = __builtin_amdgcn_ds_read_tr8_b64_v2i32((i32x2 LDS*)(cur + b_off[j][1]));
-            i32x2 b2 = __builtin_amdgcn_ds_read_tr8_b64_v2i32((i32x2 LDS*)(cur + b_off[j][2]));
-            i32x2 b3 = __builtin_amdgcn_ds_read_tr8_b64_v2i32((i32x2 LDS*)(cur + b_off[j][3]));
-            const i32x8 bf = i32x8{b0[0], b0[1], b1[0], b1[1], b2[0], b2[1], b3[0], b3[1]};
+            // B operands: transposed read t gives k = 32g + 8t + b for column q -> sub-step t
+            f16x8 bf[4];
+#pragma unroll
+            for (int t = 0; t < 4; ++t) {
+                const i32x2 raw =
+                    __builtin_amdgcn_ds_read_tr8_b64_v2i32((i32x2 LDS*)(cur + b_off[j][t]));
+                bf[t] = e4m3x8_to_f16(raw[0], raw[1]);
+            }
 #pragma unroll
             for (int i = 0; i < Cfg::FM; ++i) {
-                const f32x4 p = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
-                    af[i], bf, f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0, 0, 0, 0);
+                f32x4 p = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int t = 0; t < 4; ++t)
+                    p = __builtin_amdgcn_mfma_f32_16x16x32_f16(af[i][t], bf[t], p, 0, 0, 0);
 #pragma unroll
                 for (int r = 0; r < 4; ++r)
                     acc[i][j][r] = __builtin_fmaf(p[r], cs[i][r], acc[i][j][r]);
@@ -281,14 +308,14 @@ static hipError_t launch_cfg(const void* A_q, const float* sA, const void* B_q, 
     return hipGetLastError();
 }
 
-using CfgLarge = GemmCfg<256, 256, 4, 2>;
+using CfgLarge = GemmCfg<256, 128, 4, 2>;
 using CfgSmall = GemmCfg<128, 128, 2, 2>;
 
 hipError_t launch_gemm_fp8_blockscaled(const void* A_q, const float* sA, const void* B_q,
                                        const float* sB, void* C, int64_t M, int64_t N,
                                        int64_t K, int out_bf16, hipStream_t stream)
 {
-    if (M >= 256 && N >= 256 && N % 256 == 0)
+    if (M >= 256)
         return launch_cfg<CfgLarge>(A_q, sA, B_q, sB, C, M, N, K, out_bf16, stream);
     return launch_cfg<CfgSmall>(A_q, sA, B_q, sB, C, M, N, K, out_bf16, stream);
 }
