@@ -27,12 +27,129 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 PEAK_FP8_TFLOPS = 5000.0     # MI355X dense FP8 MFMA (no sparsity)
+PEAK_F16_TFLOPS = 2500.0     # MI355X dense FP16 MFMA (the instruction the GEMM issues)
 PEAK_HBM_GBS = 8000.0        # MI355X HBM3E
 METRIC = "block-scaled FP8 GEMM TFLOP/s (% FP8 MFMA peak); quantize GB/s (% HBM)"
 
 
 def log(msg):
     print(msg, file=sys.stderr, flush=True)
+
+
+PROFILES = os.path.join(ROOT, "profiles")
+KERNEL_SOURCES = {   # the sources each profiled kernel is built from (for staleness checks)
+    "gemm": ["fine_grained_block_fgq_amd/csrc/gemm.hip"],
+    "quant_act": ["fine_grained_block_fgq_amd/csrc/quant.hip",
+                  "fine_grained_block_fgq_amd/csrc/fgq_device.hpp"],
+}
+
+
+def source_hash(kind):
+    import hashlib
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES[kind]:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def profiled_traffic(key, kind):
+    """HBM bytes per launch from the committed counter summary, or None when the kernel's
+    source changed since the counters were taken."""
+    path = os.path.join(PROFILES, "traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f).get(key)
+    if not rec or rec.get("source_sha256") != source_hash(kind):
+        return None
+    return rec["bytes_per_launch"]
+
+
+def summarize(ktrace_dir, fetch_dir, write_dir):
+    """Write the profile summaries under profiles/ from rocprofv3 csv output directories:
+    a --kernel-trace --stats run of bench.py, and --pmc FETCH_SIZE / --pmc WRITE_SIZE runs of
+    `bench.py --mode profile` (which includes a 512 MiB copy used to calibrate both counters)."""
+    import csv
+    import glob
+
+    def rows(d, suffix):
+        f = glob.glob(os.path.join(d, "**", "*" + suffix), recursive=True)
+        if not f:
+            raise SystemExit(f"no *{suffix} under {d}")
+        with open(f[0]) as fh:
+            return list(csv.DictReader(fh))
+
+    def short(name):
+        for k in ("gemm_fp8_blockscaled_kernel", "quant_act_1x128_kernel",
+                  "quant_weight_128x128_kernel", "vectorized_elementwise_kernel"):
+            if k in name:
+                return k
+        return name[:60]
+
+    os.makedirs(PROFILES, exist_ok=True)
+    # kernel durations
+    trace = rows(ktrace_dir, "kernel_trace.csv")
+    groups = {}
+    for r in trace:
+        key = (short(r["Kernel_Name"]), int(r["Grid_Size_X"] if "Grid_Size_X" in r else r.get("Grid_Size", 0)))
+        groups.setdefault(key, []).append(int(r["End_Timestamp"]) - int(r["Start_Timestamp"]))
+    lines = [f"{'kernel':34s} {'grid':>9s} {'calls':>6s} {'avg_us':>9s} {'min_us':>9s} {'max_us':>9s}"]
+    for (name, grid), d in sorted(groups.items()):
+        lines.append(f"{name:34s} {grid:9d} {len(d):6d} {sum(d)/len(d)/1e3:9.2f} {min(d)/1e3:9.2f} {max(d)/1e3:9.2f}")
+    stats = "\n".join(lines)
+    # counters
+    def counter(d, cname):
+        acc = {}
+        for r in rows(d, "counter_collection.csv"):
+            if r["Counter_Name"] != cname:
+                continue
+            acc.setdefault((short(r["Kernel_Name"]), int(r["Grid_Size"])), []).append(float(r["Counter_Value"]))
+        return acc
+    fetch_l, write_l = counter(fetch_dir, "FETCH_SIZE"), counter(write_dir, "WRITE_SIZE")
+    # the 512 MiB elementwise dispatches are the fill of the copy's source (writes only)
+    # followed by the copies (read + write 512 MiB each): calibrate on the copies
+    fk = ("vectorized_elementwise_kernel", 33554432)
+    copy_fetch = sorted(fetch_l[fk])[1:]          # drop the fill
+    copy_write = sorted(write_l[fk])
+    fetch = {k: sum(v) / len(v) for k, v in fetch_l.items()}
+    write = {k: sum(v) / len(v) for k, v in write_l.items()}
+    fetch[fk] = sum(copy_fetch) / len(copy_fetch)
+    write[fk] = copy_write[len(copy_write) // 2]
+    copy_bytes = 512 * 2**20
+    fetch_scale = copy_bytes / (fetch[fk] * 1024)
+    write_scale = copy_bytes / (write[fk] * 1024)
+    traffic = {}
+    out = ["rocprofv3 byte counters per dispatch (KiB), scaled by the 512 MiB copy calibration",
+           f"calibration: copy FETCH_SIZE {fetch[fk]:.1f} KiB -> x{fetch_scale:.3f}; "
+           f"WRITE_SIZE {write[fk]:.1f} KiB -> x{write_scale:.3f}",
+           f"{'kernel':34s} {'grid':>9s} {'FETCH_KiB':>12s} {'WRITE_KiB':>12s} {'HBM_MB(scaled)':>15s}"]
+    for k in sorted(fetch):
+        if k not in write:
+            continue
+        b = fetch[k] * 1024 * fetch_scale + write[k] * 1024 * write_scale
+        out.append(f"{k[0]:34s} {k[1]:9d} {fetch[k]:12.1f} {write[k]:12.1f} {b/1e6:15.2f}")
+        if k == ("gemm_fp8_blockscaled_kernel", 262144):
+            traffic["gemm_fp8_blockscaled 4096^3 bf16"] = {"source_sha256": source_hash("gemm"),
+                                                          "bytes_per_launch": b}
+        qa = [kk for kk in fetch if kk[0] == "quant_act_1x128_kernel"]
+        if qa and k == max(qa, key=lambda kk: kk[1]):   # the [16384,7168] launch
+            traffic["quant_act_1x128 16384x7168"] = {"source_sha256": source_hash("quant_act"),
+                                                     "bytes_per_launch": b}
+    with open(os.path.join(PROFILES, "kernel_stats_bench_step.txt"), "w") as f:
+        f.write("command: cd /tmp && export TMPDIR=/tmp; rocprofv3 --kernel-trace --stats -f csv "
+                "-d <dir> -o run -- python3 bench.py --steps 20 --warmup 5 --no-cpu-baseline\n"
+                "summary: python3 bench.py --summarize <ktrace dir> <fetch dir> <write dir>\n\n")
+        f.write(stats + "\n")
+    with open(os.path.join(PROFILES, "hbm_traffic_counters.txt"), "w") as f:
+        f.write("commands: rocprofv3 --pmc FETCH_SIZE -f csv -d <dir> -o run -- python3 bench.py "
+                "--mode profile ; rocprofv3 --pmc WRITE_SIZE -f csv -d <dir> -o run -- python3 "
+                "bench.py --mode profile\n\n")
+        f.write("\n".join(out) + "\n")
+    with open(os.path.join(PROFILES, "traffic.json"), "w") as f:
+        json.dump(traffic, f, indent=1)
+    print(stats)
+    print("\n".join(out))
 
 
 def to_dev_bf16(bits, torch):
@@ -73,6 +190,31 @@ def cpu_baseline(A, B):
     }
 
 
+def profile_pass(torch, fgq, synth, dev, reps=3):
+    """Kernels of the hot path, a few launches each, for rocprofv3 counter runs:
+    the 4096^3 step (quantize A, quantize B, GEMM), the [16384,7168] activation quantizer
+    and a 512 MiB copy whose byte counts calibrate FETCH_SIZE/WRITE_SIZE."""
+    A_bits, B_bits, _ = synth.workload_inputs("sq4096")
+    A, B = to_dev_bf16(A_bits, torch), to_dev_bf16(B_bits, torch)
+    Aq, sA = fgq.fgq_quantize_act_1x128(A)
+    Bq, sB = fgq.fgq_quantize_weight_128x128(B)
+    C = torch.empty((4096, 4096), dtype=torch.bfloat16, device=dev)
+    X_bits, _, _ = synth.workload_inputs("actq")
+    X = to_dev_bf16(X_bits, torch)
+    Xq = torch.empty(X.shape, dtype=torch.uint8, device=dev)
+    sX = torch.empty((X.shape[0], X.shape[1] // 128), dtype=torch.float32, device=dev)
+    src = torch.ones(128 << 20, dtype=torch.float32, device=dev)   # 512 MiB
+    dst = torch.empty_like(src)
+    for _ in range(reps):
+        fgq.fgq_quantize_act_1x128(A, Aq, sA)
+        fgq.fgq_quantize_weight_128x128(B, Bq, sB)
+        fgq.fgq_gemm_fp8_blockscaled(Aq, sA, Bq, sB, C)
+        fgq.fgq_quantize_act_1x128(X, Xq, sX)
+        torch.mul(src, 1.0, out=dst)
+    torch.cuda.synchronize()
+    log("profile pass done")
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -80,7 +222,16 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--quant-reps", type=int, default=50)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--summarize", nargs=3, metavar=("KTRACE_DIR", "FETCH_DIR", "WRITE_DIR"),
+                    help="write profiles/ summaries from rocprofv3 csv output and exit")
+    ap.add_argument("--mode", choices=["bench", "profile"], default="bench",
+                    help="profile: a short pass for hardware-counter runs -- the GEMM, both "
+                         "quantizers and a plain 512 MiB copy (torch.mul by 1) as the "
+                         "calibration of the byte counters; prints no JSON")
     args = ap.parse_args()
+    if args.summarize:
+        summarize(*args.summarize)
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: the path has no multi-GPU stage here "
               "(run with --gpus 1)", file=sys.stderr)
@@ -96,6 +247,10 @@ def main():
     fgq.load()
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+
+    if args.mode == "profile":
+        profile_pass(torch, fgq, synth, dev)
+        return
 
     # ---- the step workload: 4096^3, A N(0,1), B N(0,0.02), bf16 C -----------------------
     w = synth.WORKLOADS["sq4096"]
@@ -127,19 +282,15 @@ def main():
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
-    # timed region: exactly `steps` steps, no events inside
-    t0 = time.perf_counter()
-    for _ in range(args.steps):
-        step()
-    torch.cuda.synchronize()
-    t1 = time.perf_counter()
-    ms_per_step = (t1 - t0) * 1e3 / args.steps
-
-    # per-kernel durations (HIP events on the launch stream), separate pass
+    # timed region: exactly `steps` steps; HIP events on the launch stream bracket each kernel
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
     for e in evs:
         step(e)
     torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms_per_step = (t1 - t0) * 1e3 / args.steps
     qa_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in evs]))
     qw_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in evs]))
     gm_ms = float(np.mean([e[2].elapsed_time(e[3]) for e in evs]))
@@ -196,7 +347,13 @@ def main():
             "peak": PEAK_FP8_TFLOPS,
             "unit": "TFLOP/s",
             "frac": round(gemm_tflops / PEAK_FP8_TFLOPS, 4),
-            "traffic": None,
+            "traffic": profiled_traffic("gemm_fp8_blockscaled 4096^3 bf16", "gemm"),
+            "algorithmic_bytes": int(M * K + K * N + 4 * M * (K // 128)
+                                     + 4 * (K // 128) * (N // 128) + 2 * M * N),
+            "frac_f16_peak": round(gemm_tflops / PEAK_F16_TFLOPS, 4),
+            "note": "partials use f16 MFMAs on exactly converted E4M3 operands (gfx950 FP8 "
+                    "MFMA accumulation is too coarse for the fp32 tolerance); frac_f16_peak "
+                    "is against the 2500 TFLOP/s dense f16 peak of that instruction",
         },
         "kernels_us": {"quantize_act_4096x4096": round(qa_ms * 1e3, 2),
                        "quantize_weight_4096x4096": round(qw_ms * 1e3, 2),
@@ -210,7 +367,7 @@ def main():
             "frac": round(q_gbs / PEAK_HBM_GBS, 4),
             "us": round(q_ms * 1e3, 2),
             "algorithmic_bytes": q_bytes,
-            "traffic": None,
+            "traffic": profiled_traffic("quant_act_1x128 16384x7168", "quant_act"),
         },
         "cpu_baseline": None,
     }

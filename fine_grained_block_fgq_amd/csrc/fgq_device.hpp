@@ -9,7 +9,9 @@
 // How the device computes it:
 //   * amax is an exact integer max over the bf16 magnitude bits (sign cleared): for
 //     non-NaN values the unsigned order of those bits is the order of |x|;
-//   * s = amax/448 and r = 1/s use IEEE divides once per group and lane;
+//   * s = amax/448 is reached by Markstein's correction with the rounded constant 1/448
+//     (IEEE divide for amax < 2^-100), r = 1/s by v_rcp_f32 plus one Newton step, once per
+//     group and lane;
 //   * per element, y = fl32(x/s) is reached from q = x*r with one exact-remainder
 //     correction (Markstein's quotient correction: e = q*s - x is exact by FMA, then
 //     y = q - e*r).  The negated remainder keeps the sign of zero: -0 stays -0.  Groups
@@ -22,6 +24,10 @@
 #pragma once
 #include <hip/hip_runtime.h>
 #include <stdint.h>
+
+#ifndef FGQ_FAST_SCALE
+#define FGQ_FAST_SCALE 1
+#endif
 
 namespace fgq {
 
@@ -72,8 +78,27 @@ __device__ __forceinline__ GroupScale group_scale(uint32_t amax_bits16)
 {
     float amax = __uint_as_float(amax_bits16 << 16);
     GroupScale g;
+#if FGQ_FAST_SCALE
+    // s = fl32(amax/448) by Markstein's correction with the rounded constant 1/448 (exact
+    // for normal s; tiny amax takes the IEEE divide), r = 1/s by v_rcp_f32 and one Newton
+    // step.  Both are checked over every bf16 amax by the device domain sweep.
+    if (amax >= 0x1p-100f) {
+        const float c = 1.0f / 448.0f;
+        const float q0 = amax * c;
+        const float e = __builtin_fmaf(-q0, 448.0f, amax);
+        g.s = __builtin_fmaf(e, c, q0);
+    } else {
+        g.s = amax / 448.0f;
+    }
+    {
+        const float r0 = __builtin_amdgcn_rcpf(g.s);
+        const float er = __builtin_fmaf(-g.s, r0, 1.0f);
+        g.r = (g.s == 0.0f) ? 0.0f : __builtin_fmaf(er, r0, r0);
+    }
+#else
     g.s = amax / 448.0f;
     g.r = (g.s == 0.0f) ? 0.0f : 1.0f / g.s;
+#endif
     g.slow = (g.s != 0.0f) && (g.s < 0x1p-96f);
     return g;
 }

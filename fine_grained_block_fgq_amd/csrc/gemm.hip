@@ -27,6 +27,14 @@
 //     per chunk (a wave's columns never straddle a 128-column block).
 #include "fgq_launch.hpp"
 
+// compile-time tuning knobs (defaults are the shipped configuration)
+#ifndef FGQ_SCHED
+#define FGQ_SCHED 0
+#endif
+#ifndef FGQ_SWZ
+#define FGQ_SWZ 1
+#endif
+
 namespace fgq {
 
 typedef int i32x8 __attribute__((ext_vector_type(8)));
@@ -47,9 +55,9 @@ __device__ __forceinline__ f16x8 e4m3x8_to_f16(int w0, int w1)
 }
 #define LDS __attribute__((address_space(3)))
 
-template <int BM_, int BN_, int WM_, int WN_>
+template <int BM_, int BN_, int WM_, int WN_, int STAGES_>
 struct GemmCfg {
-    static constexpr int BM = BM_, BN = BN_, WM = WM_, WN = WN_;
+    static constexpr int BM = BM_, BN = BN_, WM = WM_, WN = WN_, STAGES = STAGES_;
     static constexpr int NW = WM * WN, NT = 64 * NW;
     static constexpr int TM = BM / WM, TN = BN / WN;
     static constexpr int FM = TM / 16, FN = TN / 16;
@@ -63,6 +71,33 @@ struct GemmCfg {
     static_assert(TN <= 128 && 128 % TN == 0, "a wave's columns must sit in one 128-block");
     static_assert(TM % 16 == 0 && TN % 16 == 0 && BN >= 128 && BM % 64 == 0, "tile shape");
     static_assert(A_LOADS % NW == 0 && B_LOADS % NW == 0, "loads split evenly over waves");
+    static_assert(S_LOADS <= NW, "one scale load per wave at most");
+    static_assert(STAGES == 2 || STAGES == 3, "LDS ring depth");
+    static_assert(STAGES * STAGE <= 160 * 1024, "LDS capacity (160 KB per CU)");
+    // 16-byte column swizzles.  gfx950 LDS has 64 banks of 4 bytes (256 B per cycle): a
+    // ds_read_b128 serves 16 lanes per cycle, a ds_read_b64(_tr) 32 lanes.  A rows are 128 B
+    // (two per bank line): the 16 rows of a fragment read in one cycle take 16 distinct
+    // 16-byte slots when the column is XORed with (row/2)%8.  B rows read together by one
+    // b64 transposed read are k = 32g + 8t + 0..7 for g in {0,1}: the swizzle mixes k%8 and
+    // bit 5 of k so those 16 rows hit distinct slots too.
+    static __device__ __forceinline__ int a_swz(int row)
+    {
+#if FGQ_SWZ
+        return (row >> 1) & 7;
+#else
+        return row & 7;
+#endif
+    }
+    static __device__ __forceinline__ int b_swz(int k)
+    {
+#if FGQ_SWZ
+        return B_CHUNKS == 8 ? (((k >> 1) & 3) | (((k >> 5) & 1) << 2))
+                             : ((k & 7) | (((k >> 5) & 1) << 3));
+#else
+        return k & 7;
+#endif
+    }
+    static_assert(B_CHUNKS == 8 || B_CHUNKS == 16, "BN is 128 or 256");
     // waits: every wave issues this many direct-to-LDS loads per stage (S loads go to the
     // first S_LOADS waves); the pipeline waits with the smallest count, which is safe.
     static constexpr int MIN_LOADS = (A_LOADS + B_LOADS) / NW;
@@ -126,7 +161,7 @@ __device__ __forceinline__ void load_stage(uint8_t LDS* stage, const uint8_t* __
     for (int u = 0; u < Cfg::A_LOADS / Cfg::NW; ++u) {
         const int ia = u * Cfg::NW + wave;
         const int row = ia * 8 + (lane >> 3);
-        const int c = (lane & 7) ^ (row & 7);
+        const int c = (lane & 7) ^ Cfg::a_swz(row);
         int64_t gm = m0 + row;
         gm = gm < M ? gm : M - 1;
         dma_b128(A + gm * K + kb * 128 + c * 16, lds_addr(stage + ia * 1024));
@@ -138,7 +173,7 @@ __device__ __forceinline__ void load_stage(uint8_t LDS* stage, const uint8_t* __
         const int ib = u * Cfg::NW + wave;
         const int k = ib * Cfg::B_ROWS_PER_LOAD + lane / Cfg::B_CHUNKS;
         const int p = lane % Cfg::B_CHUNKS;
-        const int c = p ^ (k & 7);
+        const int c = p ^ Cfg::b_swz(k);
         int64_t gn = n0 + c * 16;
         gn = gn < N ? gn : N - 16;
         dma_b128(B + (kb * 128 + k) * N + gn, lds_addr(stage + Cfg::A_BYTES + ib * 1024));
@@ -151,12 +186,81 @@ __device__ __forceinline__ void load_stage(uint8_t LDS* stage, const uint8_t* __
     }
 }
 
+// One 128-K chunk of the wave's 16x16 tiles: f16 operands, four chained f16 MFMAs per
+// tile, then acc += P * (sA*sB).
+template <class Cfg>
+__device__ __forceinline__ void compute_chunk(const uint8_t LDS* cur, const int (&a_off)[Cfg::FM][2],
+                                              const int (&b_off)[Cfg::FN][4], int s_off, float sb,
+                                              f32x4 (&acc)[Cfg::FM][Cfg::FN])
+{
+    // combined scales for this lane's rows: sA[row, kb] * sB[kb, nb]
+    f32x4 cs[Cfg::FM];
+#pragma unroll
+    for (int i = 0; i < Cfg::FM; ++i) {
+        const f32x4 sa = *(const f32x4 LDS*)(cur + s_off + i * 64);
+        cs[i] = sa * sb;
+    }
+    // A operands: lane bytes 8t..8t+7 of its 32 (k = 32g + 8t + b) -> sub-step t
+    i32x4 araw[Cfg::FM][2];
+#pragma unroll
+    for (int i = 0; i < Cfg::FM; ++i) {
+        araw[i][0] = *(const i32x4 LDS*)(cur + a_off[i][0]);
+        araw[i][1] = *(const i32x4 LDS*)(cur + a_off[i][1]);
+    }
+    // B operands: transposed read t gives k = 32g + 8t + b for column q -> sub-step t
+    i32x2 braw[2][4];
+#pragma unroll
+    for (int t = 0; t < 4; ++t)
+        braw[0][t] = __builtin_amdgcn_ds_read_tr8_b64_v2i32((i32x2 LDS*)(cur + b_off[0][t]));
+    f16x8 af[Cfg::FM][4];
+#pragma unroll
+    for (int i = 0; i < Cfg::FM; ++i) {
+        af[i][0] = e4m3x8_to_f16(araw[i][0][0], araw[i][0][1]);
+        af[i][1] = e4m3x8_to_f16(araw[i][0][2], araw[i][0][3]);
+        af[i][2] = e4m3x8_to_f16(araw[i][1][0], araw[i][1][1]);
+        af[i][3] = e4m3x8_to_f16(araw[i][1][2], araw[i][1][3]);
+    }
+#pragma unroll
+    for (int j = 0; j < Cfg::FN; ++j) {
+        if (j + 1 < Cfg::FN) {
+#pragma unroll
+            for (int t = 0; t < 4; ++t)
+                braw[(j + 1) & 1][t] =
+                    __builtin_amdgcn_ds_read_tr8_b64_v2i32((i32x2 LDS*)(cur + b_off[j + 1][t]));
+        }
+        f16x8 bf[4];
+#pragma unroll
+        for (int t = 0; t < 4; ++t)
+            bf[t] = e4m3x8_to_f16(braw[j & 1][t][0], braw[j & 1][t][1]);
+        f32x4 p[Cfg::FM];
+#pragma unroll
+        for (int i = 0; i < Cfg::FM; ++i)
+            p[i] = __builtin_amdgcn_mfma_f32_16x16x32_f16(af[i][0], bf[0], f32x4{0.f, 0.f, 0.f, 0.f},
+                                                          0, 0, 0);
+#pragma unroll
+        for (int t = 1; t < 4; ++t)
+#pragma unroll
+            for (int i = 0; i < Cfg::FM; ++i)
+                p[i] = __builtin_amdgcn_mfma_f32_16x16x32_f16(af[i][t], bf[t], p[i], 0, 0, 0);
+#pragma unroll
+        for (int i = 0; i < Cfg::FM; ++i)
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+                acc[i][j][r] = __builtin_fmaf(p[i][r], cs[i][r], acc[i][j][r]);
+    }
+#if FGQ_SCHED == 1
+    __builtin_amdgcn_iglp_opt(0);
+#elif FGQ_SCHED == 2
+    __builtin_amdgcn_iglp_opt(1);
+#endif
+}
+
 template <class Cfg, bool OUT_BF16>
 __global__ __launch_bounds__(Cfg::NT) void gemm_fp8_blockscaled_kernel(
     const uint8_t* __restrict__ A, const float* __restrict__ sA, const uint8_t* __restrict__ B,
     const float* __restrict__ sB, void* __restrict__ Cout, int64_t M, int64_t N, int64_t K)
 {
-    __shared__ __attribute__((aligned(1024))) uint8_t smem_raw[2 * Cfg::STAGE];
+    __shared__ __attribute__((aligned(1024))) uint8_t smem_raw[Cfg::STAGES * Cfg::STAGE];
     uint8_t LDS* const smem = (uint8_t LDS*)smem_raw;
 
     const int lane = threadIdx.x & 63;
@@ -189,8 +293,8 @@ __global__ __launch_bounds__(Cfg::NT) void gemm_fp8_blockscaled_kernel(
 #pragma unroll
     for (int i = 0; i < Cfg::FM; ++i) {
         const int row = wm * Cfg::TM + 16 * i + q;
-        a_off[i][0] = row * 128 + (((2 * g) ^ (row & 7)) * 16);
-        a_off[i][1] = row * 128 + (((2 * g + 1) ^ (row & 7)) * 16);
+        a_off[i][0] = row * 128 + (((2 * g) ^ Cfg::a_swz(row)) * 16);
+        a_off[i][1] = row * 128 + (((2 * g + 1) ^ Cfg::a_swz(row)) * 16);
     }
     int b_off[Cfg::FN][4];
 #pragma unroll
@@ -199,7 +303,7 @@ __global__ __launch_bounds__(Cfg::NT) void gemm_fp8_blockscaled_kernel(
 #pragma unroll
         for (int t = 0; t < 4; ++t) {
             const int k = 32 * g + 8 * t + (q >> 1);
-            b_off[j][t] = Cfg::A_BYTES + k * Cfg::BN + ((ch ^ (k & 7)) * 16) + 8 * (q & 1);
+            b_off[j][t] = Cfg::A_BYTES + k * Cfg::BN + ((ch ^ Cfg::b_swz(k)) * 16) + 8 * (q & 1);
         }
     }
     const int s_off = Cfg::A_BYTES + Cfg::B_BYTES + (wm * Cfg::TM + 4 * g) * 4;
@@ -212,61 +316,29 @@ __global__ __launch_bounds__(Cfg::NT) void gemm_fp8_blockscaled_kernel(
         for (int j = 0; j < Cfg::FN; ++j)
             acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-    if (KB > 0)
-        load_stage<Cfg>(smem, A, sA, B, M, N, K, m0, n0, 0, wave, lane);
+    // prologue: the first STAGES-1 chunks in flight
+#pragma unroll
+    for (int st = 0; st < Cfg::STAGES - 1; ++st)
+        if (st < KB)
+            load_stage<Cfg>(smem + st * Cfg::STAGE, A, sA, B, M, N, K, m0, n0, st, wave, lane);
 
     for (int64_t kb = 0; kb < KB; ++kb) {
-        uint8_t LDS* cur = smem + (kb & 1) * Cfg::STAGE;
-        if (kb + 1 < KB) {
-            load_stage<Cfg>(smem + ((kb + 1) & 1) * Cfg::STAGE, A, sA, B, M, N, K, m0, n0,
-                            kb + 1, wave, lane);
+        const uint8_t LDS* cur = smem + (kb % Cfg::STAGES) * Cfg::STAGE;
+        // chunk kb has landed once only the later chunks' loads may still be outstanding
+        if (Cfg::STAGES == 3 && kb + 1 < KB)
             wait_vm<Cfg::MIN_LOADS>();
-        } else {
+        else
             wait_vm<0>();
-        }
+        // all waves: chunk kb visible, and chunk kb-1 fully read (its buffer may refill)
         lds_barrier();
-
-        // combined scales for this lane's rows: sA[row, kb] * sB[kb, nb]
+        const int64_t nxt = kb + Cfg::STAGES - 1;
+        if (nxt < KB)
+            load_stage<Cfg>(smem + (nxt % Cfg::STAGES) * Cfg::STAGE, A, sA, B, M, N, K, m0, n0,
+                            nxt, wave, lane);
         const float sb = (nb_wave < NB) ? sB[kb * NB + nb_wave] : 0.0f;
-        f32x4 cs[Cfg::FM];
-#pragma unroll
-        for (int i = 0; i < Cfg::FM; ++i) {
-            const f32x4 sa = *(const f32x4 LDS*)(cur + s_off + i * 64);
-            cs[i] = sa * sb;
-        }
-        // A operands: lane bytes 8s..8s+7 of its 32 (k = 32g + 8s + b) -> sub-step s
-        f16x8 af[Cfg::FM][4];
-#pragma unroll
-        for (int i = 0; i < Cfg::FM; ++i) {
-            const i32x4 lo = *(const i32x4 LDS*)(cur + a_off[i][0]);
-            const i32x4 hi = *(const i32x4 LDS*)(cur + a_off[i][1]);
-            af[i][0] = e4m3x8_to_f16(lo[0], lo[1]);
-            af[i][1] = e4m3x8_to_f16(lo[2], lo[3]);
-            af[i][2] = e4m3x8_to_f16(hi[0], hi[1]);
-            af[i][3] = e4m3x8_to_f16(hi[2], hi[3]);
-        }
-#pragma unroll
-        for (int j = 0; j < Cfg::FN; ++j) {
-            // B operands: transposed read t gives k = 32g + 8t + b for column q -> sub-step t
-            f16x8 bf[4];
-#pragma unroll
-            for (int t = 0; t < 4; ++t) {
-                const i32x2 raw =
-                    __builtin_amdgcn_ds_read_tr8_b64_v2i32((i32x2 LDS*)(cur + b_off[j][t]));
-                bf[t] = e4m3x8_to_f16(raw[0], raw[1]);
-            }
-#pragma unroll
-            for (int i = 0; i < Cfg::FM; ++i) {
-                f32x4 p = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                for (int t = 0; t < 4; ++t)
-                    p = __builtin_amdgcn_mfma_f32_16x16x32_f16(af[i][t], bf[t], p, 0, 0, 0);
-#pragma unroll
-                for (int r = 0; r < 4; ++r)
-                    acc[i][j][r] = __builtin_fmaf(p[r], cs[i][r], acc[i][j][r]);
-            }
-        }
-        lds_barrier();
+        compute_chunk<Cfg>(cur, a_off, b_off, s_off, sb, acc);
+        if (Cfg::STAGES == 2)
+            lds_barrier();   // chunk kb fully read before the next iteration refills it
     }
 
     // epilogue: lane holds C[16i + 4g + r][16j + q] of the wave tile
@@ -308,8 +380,14 @@ static hipError_t launch_cfg(const void* A_q, const float* sA, const void* B_q, 
     return hipGetLastError();
 }
 
-using CfgLarge = GemmCfg<256, 128, 4, 2>;
-using CfgSmall = GemmCfg<128, 128, 2, 2>;
+#ifndef FGQ_LARGE_CFG
+#define FGQ_LARGE_CFG 256, 128, 4, 2, 2
+#endif
+#ifndef FGQ_SMALL_CFG
+#define FGQ_SMALL_CFG 128, 128, 2, 2, 2
+#endif
+using CfgLarge = GemmCfg<FGQ_LARGE_CFG>;
+using CfgSmall = GemmCfg<FGQ_SMALL_CFG>;
 
 hipError_t launch_gemm_fp8_blockscaled(const void* A_q, const float* sA, const void* B_q,
                                        const float* sB, void* C, int64_t M, int64_t N,

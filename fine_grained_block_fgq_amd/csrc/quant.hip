@@ -21,10 +21,23 @@ namespace fgq {
 // bytes [16j, 16j+16) of it (8 bf16 -> 8 codes).  A wave covers 4 consecutive tiles per
 // load (1 KB, fully coalesced) and issues ACT_UNROLL such loads before using any of them.
 // ---------------------------------------------------------------------------------------
-constexpr int ACT_UNROLL = 4;
-constexpr int ACT_WAVES = 4;
+#ifndef FGQ_ACT_UNROLL
+#define FGQ_ACT_UNROLL 2
+#endif
+#ifndef FGQ_ACT_WAVES
+#define FGQ_ACT_WAVES 4
+#endif
+constexpr int ACT_UNROLL = FGQ_ACT_UNROLL;
+constexpr int ACT_WAVES = FGQ_ACT_WAVES;
 constexpr int ACT_TILES_PER_WAVE = 4 * ACT_UNROLL;
 constexpr int ACT_TILES_PER_BLOCK = ACT_WAVES * ACT_TILES_PER_WAVE;
+
+#ifndef FGQ_ACT_GRID
+#define FGQ_ACT_GRID 0
+#endif
+// workgroups launched (0: one per ACT_TILES_PER_BLOCK tiles; else at most this many, each
+// looping over the tile groups with a grid stride)
+constexpr int64_t ACT_GRID = FGQ_ACT_GRID;
 
 __global__ __launch_bounds__(64 * ACT_WAVES) void quant_act_1x128_kernel(
     const u32x4* __restrict__ X, u32x2* __restrict__ Xq, float* __restrict__ sX, int64_t T)
@@ -33,7 +46,9 @@ __global__ __launch_bounds__(64 * ACT_WAVES) void quant_act_1x128_kernel(
     const int wave = threadIdx.x >> 6;
     const int sub = lane >> 4;
     const int j = lane & 15;
-    const int64_t t0 = ((int64_t)blockIdx.x * ACT_WAVES + wave) * ACT_TILES_PER_WAVE + sub;
+    const int64_t nblocks = (T + ACT_TILES_PER_BLOCK - 1) / ACT_TILES_PER_BLOCK;
+    for (int64_t blk = blockIdx.x; blk < nblocks; blk += gridDim.x) {
+    const int64_t t0 = (blk * ACT_WAVES + wave) * ACT_TILES_PER_WAVE + sub;
 
     u32x4 v[ACT_UNROLL];
 #pragma unroll
@@ -51,6 +66,7 @@ __global__ __launch_bounds__(64 * ACT_WAVES) void quant_act_1x128_kernel(
             if (j == 0)
                 sX[t] = g.s;
         }
+    }
     }
 }
 
@@ -108,7 +124,9 @@ hipError_t launch_quant_act_1x128(const void* X, void* Xq, float* sX, int64_t M,
                                   hipStream_t stream)
 {
     const int64_t T = M * (K / 128);
-    const int64_t blocks = (T + ACT_TILES_PER_BLOCK - 1) / ACT_TILES_PER_BLOCK;
+    int64_t blocks = (T + ACT_TILES_PER_BLOCK - 1) / ACT_TILES_PER_BLOCK;
+    if (ACT_GRID > 0 && blocks > ACT_GRID)
+        blocks = ACT_GRID;
     hipLaunchKernelGGL(quant_act_1x128_kernel, dim3((unsigned)blocks), dim3(64 * ACT_WAVES), 0,
                        stream, static_cast<const u32x4*>(X), static_cast<u32x2*>(Xq), sX, T);
     return hipGetLastError();
