@@ -15,12 +15,15 @@ import torch
 
 __all__ = [
     "FgqError", "library_path", "load", "fgq_quantize_act_1x128",
-    "fgq_quantize_weight_128x128", "fgq_gemm_fp8_blockscaled", "FGQ_OUT_F32", "FGQ_OUT_BF16",
+    "fgq_quantize_weight_128x128", "fgq_gemm_fp8_blockscaled",
+    "fgq_gemm_fp8_blockscaled_variant", "FGQ_OUT_F32", "FGQ_OUT_BF16", "FGQ_GEMM_AUTO",
+    "FGQ_GEMM_WIDE_256x128", "FGQ_GEMM_WIDE_128x128", "FGQ_GEMM_NARROW_64x32",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_HERE, "libfgq.so")
 FGQ_OUT_F32, FGQ_OUT_BF16 = 0, 1
+FGQ_GEMM_AUTO, FGQ_GEMM_WIDE_256x128, FGQ_GEMM_WIDE_128x128, FGQ_GEMM_NARROW_64x32 = 0, 1, 2, 3
 _lib = None
 
 
@@ -49,6 +52,8 @@ def load() -> ctypes.CDLL:
     lib.fgq_quantize_weight_128x128.argtypes = [p, p, p, i64, i64, p]
     lib.fgq_gemm_fp8_blockscaled.restype = i32
     lib.fgq_gemm_fp8_blockscaled.argtypes = [p, p, p, p, p, i64, i64, i64, i32, p]
+    lib.fgq_gemm_fp8_blockscaled_variant.restype = i32
+    lib.fgq_gemm_fp8_blockscaled_variant.argtypes = [p, p, p, p, p, i64, i64, i64, i32, i32, p]
     lib.fgq_status_string.restype = ctypes.c_char_p
     lib.fgq_status_string.argtypes = [i32]
     lib.fgq_version.restype = i32
@@ -118,6 +123,21 @@ def fgq_gemm_fp8_blockscaled(A_q: torch.Tensor, scale_A: torch.Tensor, B_q: torc
                              scale_B: torch.Tensor, C: torch.Tensor | None = None,
                              out_dtype: torch.dtype = torch.bfloat16, stream=None):
     """C[M,N] = block-scaled A_q[M,K] @ B_q[K,N] (scales [M,K/128] and [K/128,N/128])."""
+    return _gemm("fgq_gemm_fp8_blockscaled", A_q, scale_A, B_q, scale_B, C, out_dtype, None,
+                 stream)
+
+
+def fgq_gemm_fp8_blockscaled_variant(A_q: torch.Tensor, scale_A: torch.Tensor,
+                                     B_q: torch.Tensor, scale_B: torch.Tensor,
+                                     C: torch.Tensor | None = None,
+                                     out_dtype: torch.dtype = torch.bfloat16,
+                                     variant: int = FGQ_GEMM_AUTO, stream=None):
+    """fgq_gemm_fp8_blockscaled with an explicit kernel family (FGQ_GEMM_*)."""
+    return _gemm("fgq_gemm_fp8_blockscaled_variant", A_q, scale_A, B_q, scale_B, C, out_dtype,
+                 variant, stream)
+
+
+def _gemm(fn, A_q, scale_A, B_q, scale_B, C, out_dtype, variant, stream):
     lib = load()
     M, K = A_q.shape
     K2, N = B_q.shape
@@ -128,10 +148,12 @@ def fgq_gemm_fp8_blockscaled(A_q: torch.Tensor, scale_A: torch.Tensor, B_q: torc
     code = {torch.float32: FGQ_OUT_F32, torch.bfloat16: FGQ_OUT_BF16}.get(C.dtype)
     if code is None:
         raise TypeError(f"C must be float32 or bfloat16, got {C.dtype}")
-    _check("fgq_gemm_fp8_blockscaled", lib.fgq_gemm_fp8_blockscaled(
-        _dev(A_q, "A_q", _codes_dtype(A_q), (M, K)),
-        _dev(scale_A, "scale_A", torch.float32, (M, K // 128)),
-        _dev(B_q, "B_q", _codes_dtype(B_q), (K, N)),
-        _dev(scale_B, "scale_B", torch.float32, (K // 128, N // 128)),
-        _dev(C, "C", C.dtype, (M, N)), M, N, K, code, _stream(stream)))
+    args = [_dev(A_q, "A_q", _codes_dtype(A_q), (M, K)),
+            _dev(scale_A, "scale_A", torch.float32, (M, K // 128)),
+            _dev(B_q, "B_q", _codes_dtype(B_q), (K, N)),
+            _dev(scale_B, "scale_B", torch.float32, (K // 128, N // 128)),
+            _dev(C, "C", C.dtype, (M, N)), M, N, K, code]
+    if variant is not None:
+        args.append(int(variant))
+    _check(fn, getattr(lib, fn)(*args, _stream(stream)))
     return C

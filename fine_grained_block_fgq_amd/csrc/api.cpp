@@ -38,6 +38,7 @@ const char* fgq_status_string(int status)
     case FGQ_ERR_DTYPE: return "unknown output dtype";
     case FGQ_ERR_LAUNCH: return "kernel launch failed";
     case FGQ_ERR_ALIAS: return "output overlaps another buffer";
+    case FGQ_ERR_VARIANT: return "unknown GEMM variant";
     default: return "unknown status";
     }
 }
@@ -80,16 +81,20 @@ int fgq_quantize_weight_128x128(const void* W, void* Wq, float* scale_W, int64_t
                                                           static_cast<hipStream_t>(stream)));
 }
 
-int fgq_gemm_fp8_blockscaled(const void* A_q, const float* scale_A, const void* B_q,
-                             const float* scale_B, void* C, int64_t M, int64_t N, int64_t K,
-                             int out_dtype, void* stream)
+int fgq_gemm_fp8_blockscaled_variant(const void* A_q, const float* scale_A, const void* B_q,
+                                     const float* scale_B, void* C, int64_t M, int64_t N,
+                                     int64_t K, int out_dtype, int variant, void* stream)
 {
     if (out_dtype != FGQ_OUT_F32 && out_dtype != FGQ_OUT_BF16)
         return FGQ_ERR_DTYPE;
+    if (variant < FGQ_GEMM_AUTO || variant > FGQ_GEMM_NARROW_64x32)
+        return FGQ_ERR_VARIANT;
     if (M < 0 || N < 0 || K < 0 || K % 128 != 0 || N % 128 != 0 || M > kMaxDim ||
         N > kMaxDim || K > kMaxDim)
         return FGQ_ERR_SHAPE;
     if (((M + 127) / 128) * (N / 128) > kMaxDim)
+        return FGQ_ERR_SHAPE;
+    if (variant == FGQ_GEMM_NARROW_64x32 && ((M + 63) / 64) * (N / 32) > kMaxDim)
         return FGQ_ERR_SHAPE;
     if (M == 0 || N == 0)
         return FGQ_OK;
@@ -104,8 +109,16 @@ int fgq_gemm_fp8_blockscaled(const void* A_q, const float* scale_A, const void* 
                   overlap(C, nc, scale_B, 4 * (K / 128) * (N / 128))))
         return FGQ_ERR_ALIAS;
     return launch_status(fgq::launch_gemm_fp8_blockscaled(A_q, scale_A, B_q, scale_B, C, M, N, K,
-                                                          out_dtype == FGQ_OUT_BF16,
+                                                          out_dtype == FGQ_OUT_BF16, variant,
                                                           static_cast<hipStream_t>(stream)));
+}
+
+int fgq_gemm_fp8_blockscaled(const void* A_q, const float* scale_A, const void* B_q,
+                             const float* scale_B, void* C, int64_t M, int64_t N, int64_t K,
+                             int out_dtype, void* stream)
+{
+    return fgq_gemm_fp8_blockscaled_variant(A_q, scale_A, B_q, scale_B, C, M, N, K, out_dtype,
+                                            FGQ_GEMM_AUTO, stream);
 }
 
 }  // extern "C"

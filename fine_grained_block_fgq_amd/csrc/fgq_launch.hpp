@@ -9,9 +9,13 @@ hipError_t launch_quant_act_1x128(const void* X, void* Xq, float* sX, int64_t M,
                                   hipStream_t stream);
 hipError_t launch_quant_weight_128x128(const void* W, void* Wq, float* sW, int64_t K,
                                        int64_t N, hipStream_t stream);
+// GEMM kernel families (values of fgq_gemm_variant)
+enum GemmVariant { GEMM_AUTO = 0, GEMM_WIDE_256x128 = 1, GEMM_WIDE_128x128 = 2, GEMM_NARROW = 3 };
+
 // out_bf16: 0 -> C is fp32, 1 -> C is bf16 (nearest-even)
 hipError_t launch_gemm_fp8_blockscaled(const void* A_q, const float* sA, const void* B_q,
                                        const float* sB, void* C, int64_t M, int64_t N,
-                                       int64_t K, int out_bf16, hipStream_t stream);
+                                       int64_t K, int out_bf16, int variant,
+                                       hipStream_t stream);
 
 }  // namespace fgq

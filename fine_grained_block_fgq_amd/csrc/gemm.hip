@@ -380,6 +380,189 @@ static hipError_t launch_cfg(const void* A_q, const float* sA, const void* B_q, 
     return hipGetLastError();
 }
 
+// ---------------------------------------------------------------------------------------
+// Narrow tiles for few output tiles (decode-like M, e.g. M = 128 with N = 7168: 56 tiles of
+// 128x128 would leave most of the 256 CUs idle).  A workgroup owns a BM x 32 tile and its
+// KW waves split the K chunks round-robin (wave w takes chunks w, w+KW, ...); each wave
+// stages its own chunks in a private LDS ring, so the main loop has no workgroup barrier.
+// The KW partial tiles are summed in LDS in wave order ((w0 + w1) + w2) + ..., a fixed
+// order, so results are deterministic.  The per-chunk arithmetic is that of the wide
+// kernel: f16 MFMA partials over the 128-K chunk, then acc = fma(P, sA*sB, acc).
+template <int BM_, int KW_, int STAGES_>
+struct NarrowCfg {
+    static constexpr int BM = BM_, BN = 32, KW = KW_, STAGES = STAGES_;
+    static constexpr int NT = 64 * KW;
+    static constexpr int FM = BM / 16, FN = 2;
+    static constexpr int A_BYTES = BM * 128, B_BYTES = 128 * BN, S_BYTES = 256;
+    static constexpr int STAGE = A_BYTES + B_BYTES + S_BYTES;
+    static constexpr int A_LOADS = A_BYTES / 1024, B_LOADS = B_BYTES / 1024;
+    static constexpr int LOADS = A_LOADS + B_LOADS + 1;   // per chunk and wave
+    static constexpr int RED_LD = BN + 4;                  // padded row of the reduction
+    static constexpr int LDS_BYTES = KW * STAGES * STAGE > KW * BM * RED_LD * 4
+                                         ? KW * STAGES * STAGE
+                                         : KW * BM * RED_LD * 4;
+    static_assert(BM == 32 || BM == 64, "tile rows");
+    static_assert(STAGES == 2 || STAGES == 3, "LDS ring depth");
+    static_assert(LDS_BYTES <= 160 * 1024, "LDS capacity (160 KB per CU)");
+    static_assert(LOADS < 16, "wait count range");
+    // A: same row swizzle as the wide kernel.  B rows are 32 bytes (two 16-byte halves);
+    // the half is XORed with bit 5 of k, so the two 16-lane groups of one transposed read
+    // (k and k+32) fall on disjoint banks.
+    static __device__ __forceinline__ int a_swz(int row) { return (row >> 1) & 7; }
+    static __device__ __forceinline__ int b_swz(int k) { return (k >> 5) & 1; }
+};
+
+// one wave fills its stage with chunk kb: A rows m0..m0+BM-1, B rows of the chunk for
+// columns n0..n0+31, and scale_A of the rows
+template <class Cfg>
+__device__ __forceinline__ void narrow_load(uint8_t LDS* stage, const uint8_t* __restrict__ A,
+                                            const float* __restrict__ sA,
+                                            const uint8_t* __restrict__ B, int64_t M, int64_t N,
+                                            int64_t K, int64_t m0, int64_t n0, int64_t kb,
+                                            int lane)
+{
+#pragma unroll
+    for (int u = 0; u < Cfg::A_LOADS; ++u) {
+        const int row = u * 8 + (lane >> 3);
+        const int c = (lane & 7) ^ Cfg::a_swz(row);
+        int64_t gm = m0 + row;
+        gm = gm < M ? gm : M - 1;
+        dma_b128(A + gm * K + kb * 128 + c * 16, lds_addr(stage + u * 1024));
+    }
+#pragma unroll
+    for (int u = 0; u < Cfg::B_LOADS; ++u) {
+        const int k = u * 32 + (lane >> 1);
+        const int c = (lane & 1) ^ Cfg::b_swz(k);
+        dma_b128(B + (kb * 128 + k) * N + n0 + c * 16,
+                 lds_addr(stage + Cfg::A_BYTES + u * 1024));
+    }
+    int64_t gm = m0 + lane;
+    gm = gm < M ? gm : M - 1;
+    dma_b32(sA + gm * (K / 128) + kb, lds_addr(stage + Cfg::A_BYTES + Cfg::B_BYTES));
+}
+
+template <class Cfg, bool OUT_BF16>
+__global__ __launch_bounds__(Cfg::NT) void gemm_fp8_blockscaled_narrow_kernel(
+    const uint8_t* __restrict__ A, const float* __restrict__ sA, const uint8_t* __restrict__ B,
+    const float* __restrict__ sB, void* __restrict__ Cout, int64_t M, int64_t N, int64_t K)
+{
+    __shared__ __attribute__((aligned(1024))) uint8_t smem_raw[Cfg::LDS_BYTES];
+    uint8_t LDS* const smem = (uint8_t LDS*)smem_raw;
+
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int g = lane >> 4, q = lane & 15;
+
+    // tiles: row tiles fastest, so the workgroups sharing a B column panel are neighbours;
+    // consecutive ids of one XCD form one contiguous range (ids are dealt round-robin to
+    // the 8 XCDs)
+    const int64_t tiles_m = (M + Cfg::BM - 1) / Cfg::BM;
+    const int64_t G = (int64_t)gridDim.x;
+    int64_t pid = blockIdx.x;
+    if (G % 8 == 0)
+        pid = (pid % 8) * (G / 8) + pid / 8;
+    const int64_t m0 = (pid % tiles_m) * Cfg::BM, n0 = (pid / tiles_m) * Cfg::BN;
+    const int64_t KB = K / 128, NB = N / 128, nb = n0 / 128;
+
+    uint8_t LDS* const ring = smem + wave * (Cfg::STAGES * Cfg::STAGE);
+    int a_off[Cfg::FM][2];
+#pragma unroll
+    for (int i = 0; i < Cfg::FM; ++i) {
+        const int row = 16 * i + q;
+        a_off[i][0] = row * 128 + (((2 * g) ^ Cfg::a_swz(row)) * 16);
+        a_off[i][1] = row * 128 + (((2 * g + 1) ^ Cfg::a_swz(row)) * 16);
+    }
+    int b_off[Cfg::FN][4];
+#pragma unroll
+    for (int j = 0; j < Cfg::FN; ++j)
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+            const int k = 32 * g + 8 * t + (q >> 1);
+            b_off[j][t] = Cfg::A_BYTES + k * Cfg::BN + ((j ^ Cfg::b_swz(k)) * 16) + 8 * (q & 1);
+        }
+    const int s_off = Cfg::A_BYTES + Cfg::B_BYTES + 4 * g * 4;
+
+    f32x4 acc[Cfg::FM][Cfg::FN];
+#pragma unroll
+    for (int i = 0; i < Cfg::FM; ++i)
+#pragma unroll
+        for (int j = 0; j < Cfg::FN; ++j)
+            acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    // this wave's chunks: kb = wave + c*KW, c < nc
+    const int64_t nc = wave < KB ? (KB - wave + Cfg::KW - 1) / Cfg::KW : 0;
+#pragma unroll
+    for (int st = 0; st < Cfg::STAGES - 1; ++st)
+        if (st < nc)
+            narrow_load<Cfg>(ring + st * Cfg::STAGE, A, sA, B, M, N, K, m0, n0,
+                             wave + st * Cfg::KW, lane);
+    for (int64_t c = 0; c < nc; ++c) {
+        // chunk c has landed once only the next chunk's loads may be outstanding; every
+        // LDS read of the previous chunk has returned (its stage is refilled next)
+        if (Cfg::STAGES == 3 && c + 1 < nc)
+            wait_vm<Cfg::LOADS>();
+        else
+            wait_vm<0>();
+        __builtin_amdgcn_s_waitcnt(0xC07F);
+        asm volatile("" ::: "memory");
+        const int64_t nxt = c + Cfg::STAGES - 1;
+        if (nxt < nc)
+            narrow_load<Cfg>(ring + (nxt % Cfg::STAGES) * Cfg::STAGE, A, sA, B, M, N, K, m0,
+                             n0, wave + nxt * Cfg::KW, lane);
+        const int64_t kb = wave + c * Cfg::KW;
+        const float sb = sB[kb * NB + nb];
+        compute_chunk<Cfg>(ring + (c % Cfg::STAGES) * Cfg::STAGE, a_off, b_off, s_off, sb, acc);
+    }
+
+    // sum the KW partial tiles in wave order, then store coalesced
+    __syncthreads();
+    float LDS* const red = (float LDS*)smem_raw;
+#pragma unroll
+    for (int i = 0; i < Cfg::FM; ++i)
+#pragma unroll
+        for (int j = 0; j < Cfg::FN; ++j)
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+                red[(wave * Cfg::BM + 16 * i + 4 * g + r) * Cfg::RED_LD + 16 * j + q] =
+                    acc[i][j][r];
+    __syncthreads();
+#pragma unroll
+    for (int e0 = 0; e0 < Cfg::BM * Cfg::BN; e0 += Cfg::NT) {
+        const int e = e0 + (int)threadIdx.x;
+        const int row = e / Cfg::BN, col = e % Cfg::BN;
+        float v = red[row * Cfg::RED_LD + col];
+#pragma unroll
+        for (int w = 1; w < Cfg::KW; ++w)
+            v += red[(w * Cfg::BM + row) * Cfg::RED_LD + col];
+        const int64_t grow = m0 + row;
+        if (grow < M) {
+            if (OUT_BF16)
+                static_cast<__bf16*>(Cout)[grow * N + n0 + col] = (__bf16)v;
+            else
+                static_cast<float*>(Cout)[grow * N + n0 + col] = v;
+        }
+    }
+}
+
+template <class Cfg>
+static hipError_t launch_narrow(const void* A_q, const float* sA, const void* B_q,
+                                const float* sB, void* C, int64_t M, int64_t N, int64_t K,
+                                int out_bf16, hipStream_t stream)
+{
+    const int64_t tiles = ((M + Cfg::BM - 1) / Cfg::BM) * (N / Cfg::BN);
+    if (out_bf16)
+        hipLaunchKernelGGL((gemm_fp8_blockscaled_narrow_kernel<Cfg, true>),
+                           dim3((unsigned)tiles), dim3(Cfg::NT), 0, stream,
+                           static_cast<const uint8_t*>(A_q), sA,
+                           static_cast<const uint8_t*>(B_q), sB, C, M, N, K);
+    else
+        hipLaunchKernelGGL((gemm_fp8_blockscaled_narrow_kernel<Cfg, false>),
+                           dim3((unsigned)tiles), dim3(Cfg::NT), 0, stream,
+                           static_cast<const uint8_t*>(A_q), sA,
+                           static_cast<const uint8_t*>(B_q), sB, C, M, N, K);
+    return hipGetLastError();
+}
+
 #ifndef FGQ_LARGE_CFG
 #define FGQ_LARGE_CFG 256, 128, 4, 2, 2
 #endif
@@ -388,14 +571,34 @@ static hipError_t launch_cfg(const void* A_q, const float* sA, const void* B_q, 
 #endif
 using CfgLarge = GemmCfg<FGQ_LARGE_CFG>;
 using CfgSmall = GemmCfg<FGQ_SMALL_CFG>;
+#ifndef FGQ_NARROW_CFG
+#define FGQ_NARROW_CFG 64, 4, 2
+#endif
+using CfgNarrow = NarrowCfg<FGQ_NARROW_CFG>;
 
 hipError_t launch_gemm_fp8_blockscaled(const void* A_q, const float* sA, const void* B_q,
                                        const float* sB, void* C, int64_t M, int64_t N,
-                                       int64_t K, int out_bf16, hipStream_t stream)
+                                       int64_t K, int out_bf16, int variant,
+                                       hipStream_t stream)
 {
-    if (M >= 256)
+    if (variant == GEMM_AUTO) {
+        // wide tiles while they fill the 256 CUs at least once, else narrow tiles
+        const int64_t tiles_large = ((M + CfgLarge::BM - 1) / CfgLarge::BM) * (N / CfgLarge::BN);
+        const int64_t tiles_small = ((M + CfgSmall::BM - 1) / CfgSmall::BM) * (N / CfgSmall::BN);
+        variant = (M >= 256 && tiles_large >= 256) ? GEMM_WIDE_256x128
+                  : tiles_small >= 256             ? GEMM_WIDE_128x128
+                                                   : GEMM_NARROW;
+    }
+    switch (variant) {
+    case GEMM_WIDE_256x128:
         return launch_cfg<CfgLarge>(A_q, sA, B_q, sB, C, M, N, K, out_bf16, stream);
-    return launch_cfg<CfgSmall>(A_q, sA, B_q, sB, C, M, N, K, out_bf16, stream);
+    case GEMM_WIDE_128x128:
+        return launch_cfg<CfgSmall>(A_q, sA, B_q, sB, C, M, N, K, out_bf16, stream);
+    case GEMM_NARROW:
+        return launch_narrow<CfgNarrow>(A_q, sA, B_q, sB, C, M, N, K, out_bf16, stream);
+    default:
+        return hipErrorInvalidValue;
+    }
 }
 
 }  // namespace fgq

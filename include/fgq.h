@@ -43,7 +43,8 @@ typedef enum {
     FGQ_ERR_ALIGN = -3,  /* a pointer is not 16-byte aligned */
     FGQ_ERR_DTYPE = -4,  /* unknown out_dtype */
     FGQ_ERR_LAUNCH = -5, /* the HIP launch failed (hipGetLastError) */
-    FGQ_ERR_ALIAS = -6   /* an output overlaps an input or another output */
+    FGQ_ERR_ALIAS = -6,  /* an output overlaps an input or another output */
+    FGQ_ERR_VARIANT = -7 /* unknown GEMM kernel variant */
 } fgq_status;
 
 typedef enum { FGQ_OUT_F32 = 0, FGQ_OUT_BF16 = 1 } fgq_out_dtype;
@@ -74,9 +75,10 @@ int fgq_quantize_weight_128x128(const void* W, void* Wq, float* scale_W, int64_t
  * Block-scaled FP8 GEMM:
  *   C[m,n] = sum_{kb < K/128} scale_A[m,kb] * scale_B[kb, n/128]
  *                             * sum_{k in chunk kb} dec(A_q[m,k]) * dec(B_q[k,n])
- * with the chunk partial formed by the FP8 matrix cores and every scaled partial added to
- * an fp32 accumulator (summation order differs from a serial sum: results are correct to
- * fp32 rounding, not bit-identical to any particular order).
+ * with the chunk partial formed on the matrix cores from the exactly decoded E4M3 codes
+ * and every scaled partial added to an fp32 accumulator (summation order differs from a
+ * serial sum: results are correct to fp32 rounding, not bit-identical to any particular
+ * order; a given shape, variant and input always gives the same bits).
  *   A_q     in : E4M3FN [M, K] row-major       scale_A in: fp32 [M, K/128] row-major
  *   B_q     in : E4M3FN [K, N] row-major (N contiguous)
  *   scale_B in : fp32 [K/128, N/128] row-major
@@ -88,6 +90,33 @@ int fgq_quantize_weight_128x128(const void* W, void* Wq, float* scale_W, int64_t
 int fgq_gemm_fp8_blockscaled(const void* A_q, const float* scale_A, const void* B_q,
                              const float* scale_B, void* C, int64_t M, int64_t N, int64_t K,
                              int out_dtype, void* stream);
+
+/*
+ * Kernel families of the GEMM.  Every variant computes the same function within the same
+ * tolerance; they differ in tiling:
+ *   WIDE_256x128 / WIDE_128x128: one workgroup per output tile, K walked in order;
+ *   NARROW_64x32: 64x32 tiles whose K chunks are split over the 4 waves of a workgroup
+ *                 and summed in a fixed order, for shapes with few output tiles
+ *                 (decode-like M).
+ * FGQ_GEMM_AUTO picks from the shape (wide while the wide tiles cover every CU, narrow
+ * otherwise); it is what fgq_gemm_fp8_blockscaled uses.
+ */
+typedef enum {
+    FGQ_GEMM_AUTO = 0,
+    FGQ_GEMM_WIDE_256x128 = 1,
+    FGQ_GEMM_WIDE_128x128 = 2,
+    FGQ_GEMM_NARROW_64x32 = 3
+} fgq_gemm_variant;
+
+/*
+ * fgq_gemm_fp8_blockscaled with an explicit kernel family (for tests and tuning).
+ * Arguments, requirements and errors as fgq_gemm_fp8_blockscaled; in addition an unknown
+ * `variant` gives FGQ_ERR_VARIANT, and NARROW_64x32 requires ceil(M/64) * (N/32) below
+ * 2^31.
+ */
+int fgq_gemm_fp8_blockscaled_variant(const void* A_q, const float* scale_A, const void* B_q,
+                                     const float* scale_B, void* C, int64_t M, int64_t N,
+                                     int64_t K, int out_dtype, int variant, void* stream);
 
 /* Static text for a status code. */
 const char* fgq_status_string(int status);

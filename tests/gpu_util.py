@@ -49,10 +49,14 @@ def gpu_quant_weight(bits: np.ndarray, sentinel=True):
     return Wq.cpu().numpy(), sW.cpu().numpy()
 
 
-def gpu_gemm(Aq, sA, Bq, sB, out_dtype):
+def gpu_gemm(Aq, sA, Bq, sB, out_dtype, variant=None):
     M, N = Aq.shape[0], Bq.shape[1]
     C = torch.full((M, N), float("nan"), dtype=out_dtype, device="cuda")
-    fgq.fgq_gemm_fp8_blockscaled(dev_u8(Aq), dev_f32(sA), dev_u8(Bq), dev_f32(sB), C)
+    if variant is None:
+        fgq.fgq_gemm_fp8_blockscaled(dev_u8(Aq), dev_f32(sA), dev_u8(Bq), dev_f32(sB), C)
+    else:
+        fgq.fgq_gemm_fp8_blockscaled_variant(dev_u8(Aq), dev_f32(sA), dev_u8(Bq), dev_f32(sB),
+                                             C, variant=variant)
     torch.cuda.synchronize()
     return C.float().cpu().numpy().astype(np.float64)
 

@@ -31,7 +31,7 @@ def test_library_exports_declared_symbols():
 
 def test_status_strings():
     lib = fgq.load()
-    for s in (0, -1, -2, -3, -4, -5, -6):
+    for s in (0, -1, -2, -3, -4, -5, -6, -7):
         assert lib.fgq_status_string(s)
     assert lib.fgq_status_string(-99) == b"unknown status"
 
@@ -87,3 +87,16 @@ S1, S2 = 0x40000, 0x50000
 ])
 def test_gemm_validation(args, want):
     assert fgq.load().fgq_gemm_fp8_blockscaled(*args, None) == want
+
+
+@pytest.mark.parametrize("args,want", [
+    ((P, S1, Q, S2, R, 4, 128, 128, 0, 4), -7),     # unknown variant
+    ((P, S1, Q, S2, R, 4, 128, 128, 0, -1), -7),
+    ((P, S1, Q, S2, R, 4, 128, 128, 2, 3), -4),     # dtype checked first
+    ((P, S1, Q, S2, R, 4, 100, 128, 0, 3), -2),
+    ((P, S1, Q + 8, S2, R, 4, 128, 128, 0, 1), -3),
+    ((P, S1, Q, S2, P, 4, 128, 128, 0, 2), -6),
+    ((None, None, None, None, None, 0, 128, 128, 0, 3), 0),
+])
+def test_gemm_variant_validation(args, want):
+    assert fgq.load().fgq_gemm_fp8_blockscaled_variant(*args, None) == want

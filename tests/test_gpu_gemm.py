@@ -14,6 +14,9 @@ from tests.gpu_util import free, gemm_error_ratio, gpu_gemm, log
 
 pytestmark = pytest.mark.gpu
 
+# every kernel family on every edge shape (0 = the automatic choice)
+VARIANTS = [0, 1, 2, 3]
+
 
 def random_operands(M, N, K, seed):
     rng = np.random.default_rng(seed)
@@ -40,10 +43,11 @@ def workload_operands(name):
     (256, 256, 128), (512, 512, 384), (300, 512, 256), (64, 1024, 1152), (33, 128, 0),
 ])
 @pytest.mark.parametrize("out", ["f32", "bf16"])
-def test_edge_shapes(M, N, K, out):
-    log(f"gemm edge M={M} N={N} K={K} {out}")
+@pytest.mark.parametrize("variant", VARIANTS)
+def test_edge_shapes(M, N, K, out, variant):
+    log(f"gemm edge M={M} N={N} K={K} {out} variant={variant}")
     Aq, sA, Bq, sB = random_operands(M, N, K, seed=M + 7 * N + 13 * K)
-    C = gpu_gemm(Aq, sA, Bq, sB, torch.float32 if out == "f32" else torch.bfloat16)
+    C = gpu_gemm(Aq, sA, Bq, sB, torch.float32 if out == "f32" else torch.bfloat16, variant)
     Cr, S = oracle.gemm_f64(Aq, sA, Bq, sB)
     if K == 0:
         assert np.all(C == 0)
@@ -60,14 +64,17 @@ def test_tiny_workload_full():
     assert r <= 1.0
 
 
-def test_skinny_workload_full():
+@pytest.mark.parametrize("variant", [None, 2, 3])
+def test_skinny_workload_full(variant):
     Aq, sA, Bq, sB = workload_operands("skinny")
-    log("gemm skinny 128x7168x2048 f32")
-    C = gpu_gemm(Aq, sA, Bq, sB, torch.float32)
+    log(f"gemm skinny 128x7168x2048 f32 variant={variant}")
+    C = gpu_gemm(Aq, sA, Bq, sB, torch.float32, variant)
     Cr, S = oracle.gemm_f64(Aq, sA, Bq, sB)
     r = gemm_error_ratio(C, Cr, S, False)
     log(f"  max error ratio {r:.3e}")
     assert r <= 1.0
+    # repeatable bit for bit (the split-K partials are summed in a fixed order)
+    assert np.array_equal(C, gpu_gemm(Aq, sA, Bq, sB, torch.float32, variant))
     free()
 
 
