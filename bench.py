@@ -299,6 +299,31 @@ def main():
     log(f"step {ms_per_step:.4f} ms | quant A {qa_ms*1e3:.1f} us  quant B {qw_ms*1e3:.1f} us  "
         f"GEMM {gm_ms*1e3:.1f} us = {gemm_tflops:.0f} TFLOP/s")
 
+    # ---- fused epilogue: GEMM + 1x128 quantization of C in one launch, against the two
+    # launches it replaces (GEMM with bf16 C, then the activation quantizer over C) --------
+    Cq = torch.empty((M, N), dtype=torch.uint8, device=dev)
+    sC = torch.empty((M, N // 128), dtype=torch.float32, device=dev)
+    reps = max(10, args.steps // 2)
+    fev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(reps)]
+    for r in range(reps + 3):
+        e = fev[r - 3] if r >= 3 else None
+        if e is not None:
+            e[0].record(stream)
+        fgq.fgq_gemm_fp8_blockscaled_quant(Aq, sA, Bq, sB, C, Cq, sC, stream=stream)
+        if e is not None:
+            e[1].record(stream)
+        fgq.fgq_gemm_fp8_blockscaled(Aq, sA, Bq, sB, C, stream=stream)
+        if e is not None:
+            e[2].record(stream)
+        fgq.fgq_quantize_act_1x128(C, Cq, sC, stream)
+        if e is not None:
+            e[3].record(stream)
+    torch.cuda.synchronize()
+    fused_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in fev]))
+    sep_ms = float(np.mean([e[1].elapsed_time(e[3]) for e in fev]))
+    log(f"fused GEMM+quant {fused_ms*1e3:.1f} us vs GEMM then quantize {sep_ms*1e3:.1f} us")
+    del Cq, sC
+
     # ---- standalone activation quantizer, X [16384,7168] (rotating buffers) -------------
     wq = synth.WORKLOADS["actq"]
     Mq, Kq = wq.M, wq.K
@@ -368,6 +393,12 @@ def main():
             "us": round(q_ms * 1e3, 2),
             "algorithmic_bytes": q_bytes,
             "traffic": profiled_traffic("quant_act_1x128 16384x7168", "quant_act"),
+        },
+        "fused_epilogue": {
+            "workload": "4096^3 GEMM + 1x128 E4M3 quantization of its bf16 C",
+            "fused_us": round(fused_ms * 1e3, 2),
+            "separate_us": round(sep_ms * 1e3, 2),
+            "saved_us": round((sep_ms - fused_ms) * 1e3, 2),
         },
         "cpu_baseline": None,
     }

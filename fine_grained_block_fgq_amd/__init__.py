@@ -16,7 +16,7 @@ import torch
 __all__ = [
     "FgqError", "library_path", "load", "fgq_quantize_act_1x128",
     "fgq_quantize_weight_128x128", "fgq_gemm_fp8_blockscaled",
-    "fgq_gemm_fp8_blockscaled_variant", "FGQ_OUT_F32", "FGQ_OUT_BF16", "FGQ_GEMM_AUTO",
+    "fgq_gemm_fp8_blockscaled_variant", "fgq_gemm_fp8_blockscaled_quant", "FGQ_OUT_F32", "FGQ_OUT_BF16", "FGQ_GEMM_AUTO",
     "FGQ_GEMM_WIDE_256x128", "FGQ_GEMM_WIDE_128x128", "FGQ_GEMM_NARROW_64x32",
 ]
 
@@ -54,6 +54,8 @@ def load() -> ctypes.CDLL:
     lib.fgq_gemm_fp8_blockscaled.argtypes = [p, p, p, p, p, i64, i64, i64, i32, p]
     lib.fgq_gemm_fp8_blockscaled_variant.restype = i32
     lib.fgq_gemm_fp8_blockscaled_variant.argtypes = [p, p, p, p, p, i64, i64, i64, i32, i32, p]
+    lib.fgq_gemm_fp8_blockscaled_quant.restype = i32
+    lib.fgq_gemm_fp8_blockscaled_quant.argtypes = [p, p, p, p, p, p, p, i64, i64, i64, p]
     lib.fgq_status_string.restype = ctypes.c_char_p
     lib.fgq_status_string.argtypes = [i32]
     lib.fgq_version.restype = i32
@@ -157,3 +159,30 @@ def _gemm(fn, A_q, scale_A, B_q, scale_B, C, out_dtype, variant, stream):
         args.append(int(variant))
     _check(fn, getattr(lib, fn)(*args, _stream(stream)))
     return C
+
+
+def fgq_gemm_fp8_blockscaled_quant(A_q: torch.Tensor, scale_A: torch.Tensor, B_q: torch.Tensor,
+                                   scale_B: torch.Tensor, C: torch.Tensor | None = None,
+                                   C_q: torch.Tensor | None = None,
+                                   scale_C: torch.Tensor | None = None, stream=None):
+    """(C bf16, C_q, scale_C): the bf16 GEMM and the 1x128 quantization of that C, fused."""
+    lib = load()
+    M, K = A_q.shape
+    K2, N = B_q.shape
+    if K2 != K:
+        raise ValueError(f"A_q is [{M},{K}] but B_q is [{K2},{N}]")
+    dev = A_q.device
+    if C is None:
+        C = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+    if C_q is None:
+        C_q = torch.empty((M, N), dtype=torch.uint8, device=dev)
+    if scale_C is None:
+        scale_C = torch.empty((M, N // 128), dtype=torch.float32, device=dev)
+    _check("fgq_gemm_fp8_blockscaled_quant", lib.fgq_gemm_fp8_blockscaled_quant(
+        _dev(A_q, "A_q", _codes_dtype(A_q), (M, K)),
+        _dev(scale_A, "scale_A", torch.float32, (M, K // 128)),
+        _dev(B_q, "B_q", _codes_dtype(B_q), (K, N)),
+        _dev(scale_B, "scale_B", torch.float32, (K // 128, N // 128)),
+        _dev(C, "C", torch.bfloat16, (M, N)), _dev(C_q, "C_q", _codes_dtype(C_q), (M, N)),
+        _dev(scale_C, "scale_C", torch.float32, (M, N // 128)), M, N, K, _stream(stream)))
+    return C, C_q, scale_C

@@ -121,4 +121,38 @@ int fgq_gemm_fp8_blockscaled(const void* A_q, const float* scale_A, const void* 
                                             FGQ_GEMM_AUTO, stream);
 }
 
+int fgq_gemm_fp8_blockscaled_quant(const void* A_q, const float* scale_A, const void* B_q,
+                                   const float* scale_B, void* C, void* C_q, float* scale_C,
+                                   int64_t M, int64_t N, int64_t K, void* stream)
+{
+    if (M < 0 || N < 0 || K < 0 || K % 128 != 0 || N % 128 != 0 || M > kMaxDim ||
+        N > kMaxDim || K > kMaxDim)
+        return FGQ_ERR_SHAPE;
+    if (((M + 127) / 128) * (N / 128) > kMaxDim)
+        return FGQ_ERR_SHAPE;
+    if (M == 0 || N == 0)
+        return FGQ_OK;
+    if (!C || !C_q || !scale_C || (K > 0 && (!A_q || !scale_A || !B_q || !scale_B)))
+        return FGQ_ERR_NULL;
+    if (misaligned(C) || misaligned(C_q) || misaligned(scale_C) ||
+        (K > 0 && (misaligned(A_q) || misaligned(scale_A) || misaligned(B_q) ||
+                   misaligned(scale_B))))
+        return FGQ_ERR_ALIGN;
+    const int64_t nc = 2 * M * N, nq = M * N, ns = 4 * M * (N / 128);
+    const void* outs[3] = {C, C_q, scale_C};
+    const int64_t nout[3] = {nc, nq, ns};
+    for (int o = 0; o < 3; ++o) {
+        for (int p = o + 1; p < 3; ++p)
+            if (overlap(outs[o], nout[o], outs[p], nout[p]))
+                return FGQ_ERR_ALIAS;
+        if (K > 0 && (overlap(outs[o], nout[o], A_q, M * K) ||
+                      overlap(outs[o], nout[o], B_q, K * N) ||
+                      overlap(outs[o], nout[o], scale_A, 4 * M * (K / 128)) ||
+                      overlap(outs[o], nout[o], scale_B, 4 * (K / 128) * (N / 128))))
+            return FGQ_ERR_ALIAS;
+    }
+    return launch_status(fgq::launch_gemm_fp8_blockscaled_quant(
+        A_q, scale_A, B_q, scale_B, C, C_q, scale_C, M, N, K, static_cast<hipStream_t>(stream)));
+}
+
 }  // extern "C"

@@ -18,4 +18,10 @@ hipError_t launch_gemm_fp8_blockscaled(const void* A_q, const float* sA, const v
                                        int64_t K, int out_bf16, int variant,
                                        hipStream_t stream);
 
+// C = bf16 GEMM result, plus its 1x128 E4M3 quantization (Cq [M,N], sC [M,N/128])
+hipError_t launch_gemm_fp8_blockscaled_quant(const void* A_q, const float* sA, const void* B_q,
+                                             const float* sB, void* C, void* Cq, float* sC,
+                                             int64_t M, int64_t N, int64_t K,
+                                             hipStream_t stream);
+
 }  // namespace fgq

@@ -25,6 +25,7 @@
 //     each 16-lane group;
 //   * scale_A rows of the tile ride along in the LDS stage; scale_B is one scalar per wave
 //     per chunk (a wave's columns never straddle a 128-column block).
+#include "fgq_device.hpp"
 #include "fgq_launch.hpp"
 
 // compile-time tuning knobs (defaults are the shipped configuration)
@@ -255,10 +256,61 @@ __device__ __forceinline__ void compute_chunk(const uint8_t LDS* cur, const int 
 #endif
 }
 
-template <class Cfg, bool OUT_BF16>
+// Fused epilogue: the tile's bf16 results are staged in LDS, then every 1x128 row group is
+// written to C and quantized exactly as the activation quantizer does it (same amax, scale
+// and E4M3 conversion routines), giving the next layer's codes and scales without a second
+// pass over C.  Page "Kernel Fusion" (overview: one launch instead of a global-memory round
+// trip) applied to the 1x128 activation rule of page "Fine-Grained FP8/FP4 Quantization",
+// section "Scaling Granularities".
+template <class Cfg>
+__device__ __forceinline__ void store_quant_tile(uint8_t LDS* smem,
+                                                 const f32x4 (&acc)[Cfg::FM][Cfg::FN],
+                                                 __bf16* __restrict__ C, uint8_t* __restrict__ Cq,
+                                                 float* __restrict__ sC, int64_t M, int64_t N,
+                                                 int64_t m0, int64_t n0, int wm, int wn, int g,
+                                                 int q)
+{
+    // staged row: BN bf16 plus 16 bytes, so the four row groups 4g+r written together by a
+    // wave land on different banks
+    constexpr int LD = Cfg::BN * 2 + 16;
+    static_assert(Cfg::BM * LD <= Cfg::STAGES * Cfg::STAGE, "staged tile fits the LDS ring");
+#pragma unroll
+    for (int i = 0; i < Cfg::FM; ++i)
+#pragma unroll
+        for (int j = 0; j < Cfg::FN; ++j)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int row = wm * Cfg::TM + 16 * i + 4 * g + r;
+                const int col = wn * Cfg::TN + 16 * j + q;
+                *(__bf16 LDS*)(smem + row * LD + col * 2) = (__bf16)acc[i][j][r];
+            }
+    lds_barrier();
+    // one 16-lane DPP row per 1x128 group: 16 bytes (8 values) per lane
+    constexpr int GPR = Cfg::BN / 128;
+    const int l16 = threadIdx.x & 15;
+    const int64_t NB = N / 128;
+#pragma unroll
+    for (int g0 = 0; g0 < Cfg::BM * GPR; g0 += Cfg::NT / 16) {
+        const int grp = g0 + (int)(threadIdx.x >> 4);
+        const int row = grp / GPR, cg = grp % GPR;
+        const u32x4 v = *(const u32x4 LDS*)(smem + row * LD + cg * 256 + l16 * 16);
+        const GroupScale gs = group_scale(row16_max(absmax_bits8(v)));
+        const u32x2 codes = quantize8(v, gs);
+        const int64_t grow = m0 + row, gcol = n0 + cg * 128 + l16 * 8;
+        if (grow < M && gcol < N) {
+            *(u32x4*)(C + grow * N + gcol) = v;
+            *(u32x2*)(Cq + grow * N + gcol) = codes;
+            if (l16 == 0)
+                sC[grow * NB + (n0 / 128 + cg)] = gs.s;
+        }
+    }
+}
+
+template <class Cfg, bool OUT_BF16, bool FUSE = false>
 __global__ __launch_bounds__(Cfg::NT) void gemm_fp8_blockscaled_kernel(
     const uint8_t* __restrict__ A, const float* __restrict__ sA, const uint8_t* __restrict__ B,
-    const float* __restrict__ sB, void* __restrict__ Cout, int64_t M, int64_t N, int64_t K)
+    const float* __restrict__ sB, void* __restrict__ Cout, int64_t M, int64_t N, int64_t K,
+    uint8_t* __restrict__ Cq = nullptr, float* __restrict__ sC = nullptr)
 {
     __shared__ __attribute__((aligned(1024))) uint8_t smem_raw[Cfg::STAGES * Cfg::STAGE];
     uint8_t LDS* const smem = (uint8_t LDS*)smem_raw;
@@ -322,6 +374,10 @@ __global__ __launch_bounds__(Cfg::NT) void gemm_fp8_blockscaled_kernel(
         if (st < KB)
             load_stage<Cfg>(smem + st * Cfg::STAGE, A, sA, B, M, N, K, m0, n0, st, wave, lane);
 
+    // scale_B of the wave's column block, loaded one chunk ahead: the scalar load then
+    // completes under the LDS barrier's wait instead of stalling the chunk's LDS reads
+    const float* const sB_col = sB + (nb_wave < NB ? nb_wave : NB - 1);
+    float sb_next = KB > 0 ? sB_col[0] : 0.0f;
     for (int64_t kb = 0; kb < KB; ++kb) {
         const uint8_t LDS* cur = smem + (kb % Cfg::STAGES) * Cfg::STAGE;
         // chunk kb has landed once only the later chunks' loads may still be outstanding
@@ -331,16 +387,24 @@ __global__ __launch_bounds__(Cfg::NT) void gemm_fp8_blockscaled_kernel(
             wait_vm<0>();
         // all waves: chunk kb visible, and chunk kb-1 fully read (its buffer may refill)
         lds_barrier();
+        const float sb = sb_next;
         const int64_t nxt = kb + Cfg::STAGES - 1;
         if (nxt < KB)
             load_stage<Cfg>(smem + (nxt % Cfg::STAGES) * Cfg::STAGE, A, sA, B, M, N, K, m0, n0,
                             nxt, wave, lane);
-        const float sb = (nb_wave < NB) ? sB[kb * NB + nb_wave] : 0.0f;
+        if (kb + 1 < KB)
+            sb_next = sB_col[(kb + 1) * NB];
         compute_chunk<Cfg>(cur, a_off, b_off, s_off, sb, acc);
         if (Cfg::STAGES == 2)
             lds_barrier();   // chunk kb fully read before the next iteration refills it
     }
 
+    if (FUSE) {
+        lds_barrier();   // every wave is done with the ring: it becomes the staging tile
+        store_quant_tile<Cfg>(smem, acc, static_cast<__bf16*>(Cout), Cq, sC, M, N, m0, n0, wm,
+                              wn, g, q);
+        return;
+    }
     // epilogue: lane holds C[16i + 4g + r][16j + q] of the wave tile
 #pragma unroll
     for (int i = 0; i < Cfg::FM; ++i) {
@@ -563,6 +627,19 @@ static hipError_t launch_narrow(const void* A_q, const float* sA, const void* B_
     return hipGetLastError();
 }
 
+template <class Cfg>
+static hipError_t launch_fused(const void* A_q, const float* sA, const void* B_q, const float* sB,
+                               void* C, void* Cq, float* sC, int64_t M, int64_t N, int64_t K,
+                               hipStream_t stream)
+{
+    const int64_t tiles = ((M + Cfg::BM - 1) / Cfg::BM) * ((N + Cfg::BN - 1) / Cfg::BN);
+    hipLaunchKernelGGL((gemm_fp8_blockscaled_kernel<Cfg, true, true>), dim3((unsigned)tiles),
+                       dim3(Cfg::NT), 0, stream, static_cast<const uint8_t*>(A_q), sA,
+                       static_cast<const uint8_t*>(B_q), sB, C, M, N, K,
+                       static_cast<uint8_t*>(Cq), sC);
+    return hipGetLastError();
+}
+
 #ifndef FGQ_LARGE_CFG
 #define FGQ_LARGE_CFG 256, 128, 4, 2, 2
 #endif
@@ -599,6 +676,17 @@ hipError_t launch_gemm_fp8_blockscaled(const void* A_q, const float* sA, const v
     default:
         return hipErrorInvalidValue;
     }
+}
+
+hipError_t launch_gemm_fp8_blockscaled_quant(const void* A_q, const float* sA, const void* B_q,
+                                             const float* sB, void* C, void* Cq, float* sC,
+                                             int64_t M, int64_t N, int64_t K, hipStream_t stream)
+{
+    // whole 128-column groups per workgroup: the wide tiles only
+    const int64_t tiles_large = ((M + CfgLarge::BM - 1) / CfgLarge::BM) * (N / CfgLarge::BN);
+    if (M >= 256 && tiles_large >= 256)
+        return launch_fused<CfgLarge>(A_q, sA, B_q, sB, C, Cq, sC, M, N, K, stream);
+    return launch_fused<CfgSmall>(A_q, sA, B_q, sB, C, Cq, sC, M, N, K, stream);
 }
 
 }  // namespace fgq

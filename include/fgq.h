@@ -118,6 +118,20 @@ int fgq_gemm_fp8_blockscaled_variant(const void* A_q, const float* scale_A, cons
                                      const float* scale_B, void* C, int64_t M, int64_t N,
                                      int64_t K, int out_dtype, int variant, void* stream);
 
+/*
+ * Block-scaled FP8 GEMM with the next layer's activation quantization fused into its
+ * epilogue (page "Kernel Fusion": one launch instead of a round trip through memory):
+ *   C       out: bf16 [M, N], the GEMM of fgq_gemm_fp8_blockscaled with FGQ_OUT_BF16
+ *   C_q     out: E4M3FN [M, N]         } exactly fgq_quantize_act_1x128 applied to the C
+ *   scale_C out: fp32 [M, N/128]        } written here (bit for bit)
+ * Arguments, requirements and errors as fgq_gemm_fp8_blockscaled; none of the three outputs
+ * may overlap each other or an input.  Always runs the wide kernel family (each workgroup
+ * owns whole 128-column groups of its rows).
+ */
+int fgq_gemm_fp8_blockscaled_quant(const void* A_q, const float* scale_A, const void* B_q,
+                                   const float* scale_B, void* C, void* C_q, float* scale_C,
+                                   int64_t M, int64_t N, int64_t K, void* stream);
+
 /* Static text for a status code. */
 const char* fgq_status_string(int status);
 

@@ -100,3 +100,18 @@ def test_gemm_validation(args, want):
 ])
 def test_gemm_variant_validation(args, want):
     assert fgq.load().fgq_gemm_fp8_blockscaled_variant(*args, None) == want
+
+
+T1 = 0x60000
+
+
+@pytest.mark.parametrize("args,want", [
+    ((P, S1, Q, S2, R, T1, 0x70000, 4, 100, 128), -2),
+    ((P, S1, Q, S2, R, None, 0x70000, 4, 128, 128), -1),
+    ((P, S1, Q, S2, R, T1 + 8, 0x70000, 4, 128, 128), -3),
+    ((P, S1, Q, S2, R, R + 64, 0x70000, 4, 128, 128), -6),   # codes overlap C
+    ((P, S1, Q, S2, R, T1, P + 16, 4, 128, 128), -6),        # scales overlap A_q
+    ((None,) * 7 + (0, 128, 128), 0),
+])
+def test_gemm_quant_validation(args, want):
+    assert fgq.load().fgq_gemm_fp8_blockscaled_quant(*args, None) == want
