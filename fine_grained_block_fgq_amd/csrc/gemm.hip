@@ -35,6 +35,9 @@
 #ifndef FGQ_SWZ
 #define FGQ_SWZ 1
 #endif
+#ifndef FGQ_STAGED_STORE
+#define FGQ_STAGED_STORE 1
+#endif
 
 namespace fgq {
 
@@ -262,7 +265,7 @@ __device__ __forceinline__ void compute_chunk(const uint8_t LDS* cur, const int 
 // pass over C.  Page "Kernel Fusion" (overview: one launch instead of a global-memory round
 // trip) applied to the 1x128 activation rule of page "Fine-Grained FP8/FP4 Quantization",
 // section "Scaling Granularities".
-template <class Cfg>
+template <class Cfg, bool QUANT>
 __device__ __forceinline__ void store_quant_tile(uint8_t LDS* smem,
                                                  const f32x4 (&acc)[Cfg::FM][Cfg::FN],
                                                  __bf16* __restrict__ C, uint8_t* __restrict__ Cq,
@@ -294,15 +297,18 @@ __device__ __forceinline__ void store_quant_tile(uint8_t LDS* smem,
         const int grp = g0 + (int)(threadIdx.x >> 4);
         const int row = grp / GPR, cg = grp % GPR;
         const u32x4 v = *(const u32x4 LDS*)(smem + row * LD + cg * 256 + l16 * 16);
-        const GroupScale gs = group_scale(row16_max(absmax_bits8(v)));
-        const u32x2 codes = quantize8(v, gs);
         const int64_t grow = m0 + row, gcol = n0 + cg * 128 + l16 * 8;
-        if (grow < M && gcol < N) {
-            *(u32x4*)(C + grow * N + gcol) = v;
-            *(u32x2*)(Cq + grow * N + gcol) = codes;
-            if (l16 == 0)
-                sC[grow * NB + (n0 / 128 + cg)] = gs.s;
+        if (QUANT) {
+            const GroupScale gs = group_scale(row16_max(absmax_bits8(v)));
+            const u32x2 codes = quantize8(v, gs);
+            if (grow < M && gcol < N) {
+                *(u32x2*)(Cq + grow * N + gcol) = codes;
+                if (l16 == 0)
+                    sC[grow * NB + (n0 / 128 + cg)] = gs.s;
+            }
         }
+        if (grow < M && gcol < N)
+            *(u32x4*)(C + grow * N + gcol) = v;
     }
 }
 
@@ -399,12 +405,15 @@ __global__ __launch_bounds__(Cfg::NT) void gemm_fp8_blockscaled_kernel(
             lds_barrier();   // chunk kb fully read before the next iteration refills it
     }
 
-    if (FUSE) {
+    if (FUSE || (OUT_BF16 && FGQ_STAGED_STORE)) {
+        // bf16 C leaves through an LDS-staged tile: 16-byte row-contiguous stores (and, fused,
+        // the quantization of every row group)
         lds_barrier();   // every wave is done with the ring: it becomes the staging tile
-        store_quant_tile<Cfg>(smem, acc, static_cast<__bf16*>(Cout), Cq, sC, M, N, m0, n0, wm,
-                              wn, g, q);
+        store_quant_tile<Cfg, FUSE>(smem, acc, static_cast<__bf16*>(Cout), Cq, sC, M, N, m0,
+                                    n0, wm, wn, g, q);
         return;
     }
+    static_assert(!FUSE || OUT_BF16, "the fused epilogue writes bf16 C");
     // epilogue: lane holds C[16i + 4g + r][16j + q] of the wave tile
 #pragma unroll
     for (int i = 0; i < Cfg::FM; ++i) {
