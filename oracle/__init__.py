@@ -57,6 +57,12 @@ def _load():
     lib.oracle_quantize_act_1x128.argtypes = [p, p, p, i64, i64, i64, i64]
     lib.oracle_quantize_weight_128x128.restype = ctypes.c_int
     lib.oracle_quantize_weight_128x128.argtypes = [p, p, p, i64, i64, i64, i64]
+    lib.oracle_ue8m0_decode.restype = ctypes.c_double
+    lib.oracle_ue8m0_decode.argtypes = [ctypes.c_uint8]
+    lib.oracle_quantize_act_1x128_ue8m0.restype = ctypes.c_int
+    lib.oracle_quantize_act_1x128_ue8m0.argtypes = [p, p, p, i64, i64, i64, i64]
+    lib.oracle_quantize_weight_128x128_ue8m0.restype = ctypes.c_int
+    lib.oracle_quantize_weight_128x128_ue8m0.argtypes = [p, p, p, i64, i64, i64, i64]
     lib.oracle_gemm_f64.restype = ctypes.c_int
     lib.oracle_gemm_f64.argtypes = [p, p, p, p, i64, i64, i64, p, p, i64, i64]
     lib.oracle_gemm_f64_at.restype = ctypes.c_int
@@ -137,6 +143,46 @@ def quantize_weight(W_bits: np.ndarray, nthreads: int | None = None):
     sW = np.empty((K // 128, N // 128), dtype=np.float32)
     nt = nthreads or threads()
     _run(lambda a, b: lib.oracle_quantize_weight_128x128(_ptr(W), _ptr(Wq), _ptr(sW), K, N, a, b),
+         _split(K // 128, nt * 2), nt)
+    return Wq, sW
+
+
+def ue8m0_decode(e) -> np.ndarray:
+    """fp32 value 2^(e-127) of each UE8M0 byte (exact; NaN for 255), by the oracle."""
+    lib = _load()
+    e = np.asarray(e, dtype=np.uint8)
+    table = np.array([lib.oracle_ue8m0_decode(c) for c in range(256)], dtype=np.float64)
+    return table[e].astype(np.float32)
+
+
+def quantize_act_ue8m0(X_bits: np.ndarray, nthreads: int | None = None):
+    """1x128 activation quantization with UE8M0 scales -> (codes [M,K], exponents [M,K/128])."""
+    lib = _load()
+    X = np.ascontiguousarray(X_bits, dtype=np.uint16)
+    M, K = X.shape
+    if K % 128:
+        raise ValueError("K must be a multiple of 128")
+    Xq = np.empty((M, K), dtype=np.uint8)
+    sX = np.empty((M, K // 128), dtype=np.uint8)
+    nt = nthreads or threads()
+    _run(lambda a, b: lib.oracle_quantize_act_1x128_ue8m0(_ptr(X), _ptr(Xq), _ptr(sX), M, K, a,
+                                                         b),
+         _split(M, nt * 4), nt)
+    return Xq, sX
+
+
+def quantize_weight_ue8m0(W_bits: np.ndarray, nthreads: int | None = None):
+    """128x128 weight quantization with UE8M0 scales -> (codes [K,N], exponents [K/128,N/128])."""
+    lib = _load()
+    W = np.ascontiguousarray(W_bits, dtype=np.uint16)
+    K, N = W.shape
+    if K % 128 or N % 128:
+        raise ValueError("K and N must be multiples of 128")
+    Wq = np.empty((K, N), dtype=np.uint8)
+    sW = np.empty((K // 128, N // 128), dtype=np.uint8)
+    nt = nthreads or threads()
+    _run(lambda a, b: lib.oracle_quantize_weight_128x128_ue8m0(_ptr(W), _ptr(Wq), _ptr(sW), K, N,
+                                                              a, b),
          _split(K // 128, nt * 2), nt)
     return Wq, sW
 

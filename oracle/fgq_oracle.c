@@ -243,6 +243,89 @@ int oracle_gemm_f64_at(const uint8_t *Aq, const float *sA, const uint8_t *Bq, co
     return 0;
 }
 
+/* ------------------------------------------------------------------------------------ */
+/* UE8M0 power-of-two scales (page "Fine-Grained FP8/FP4 Quantization", section           */
+/* "Blackwell: Native Block Scaling": an unsigned 8-bit exponent e encodes 2^(e-127); and */
+/* table "UE8M0 vs E4M3 Scale Formats").  The page gives the format, not the rule that    */
+/* picks e from a group; the reading used here: the smallest power of two that lets the  */
+/* group's amax reach at most 448 (so no code saturates), i.e. the smallest e in 0..254   */
+/* with 448 * 2^(e-127) >= amax, e = 0 when even 2^-127 is more than enough (tiny or      */
+/* all-zero groups).  Same 1x128 / 128x128 groups and code rule as the fp32-scale path:   */
+/* code = ENC(fl32(x / s)) with s = 2^(e-127).  e = 255 is not produced (NaN in the OCP   */
+/* microscaling definition of E8M0).                                                      */
+/* ------------------------------------------------------------------------------------ */
+
+/* Value of one UE8M0 scale byte (NaN for 255). */
+double oracle_ue8m0_decode(uint8_t e)
+{
+    if (e == 255)
+        return NAN;
+    return ldexp(1.0, (int)e - 127);
+}
+
+/* The exponent byte of a group with the given amax: walk e upward; 448 * 2^(e-127) is
+ * exact in binary64, so every comparison is exact. */
+static uint8_t ue8m0_exponent(double amax)
+{
+    int e = 0;
+    while (e < 254 && 448.0 * ldexp(1.0, e - 127) < amax)
+        ++e;
+    return (uint8_t)e;
+}
+
+/* Quantize one group (index list) with a UE8M0 scale; returns the exponent byte. */
+static uint8_t quantize_group_ue8m0(const uint16_t *x, const int64_t *idx, int64_t n,
+                                    uint8_t *q)
+{
+    float amax = 0.0f;
+    for (int64_t i = 0; i < n; ++i) {
+        float v = fabsf(bf16_to_f32(x[idx[i]]));
+        if (v > amax)
+            amax = v;
+    }
+    uint8_t e = ue8m0_exponent((double)amax);
+    float s = (float)oracle_ue8m0_decode(e);   /* exact: 2^-127 .. 2^127 are binary32 values */
+    for (int64_t i = 0; i < n; ++i)
+        q[idx[i]] = oracle_e4m3_encode(bf16_to_f32(x[idx[i]]) / s);
+    return e;
+}
+
+/* 1x128 activation quantization with UE8M0 scales: sX is uint8 [M, K/128]. */
+int oracle_quantize_act_1x128_ue8m0(const uint16_t *X, uint8_t *Xq, uint8_t *sX, int64_t M,
+                                    int64_t K, int64_t m0, int64_t m1)
+{
+    if (M < 0 || K < 0 || K % 128 != 0 || m0 < 0 || m1 > M || m0 > m1)
+        return -1;
+    int64_t KB = K / 128;
+    int64_t idx[128];
+    for (int64_t m = m0; m < m1; ++m)
+        for (int64_t kb = 0; kb < KB; ++kb) {
+            for (int64_t j = 0; j < 128; ++j)
+                idx[j] = m * K + kb * 128 + j;
+            sX[m * KB + kb] = quantize_group_ue8m0(X, idx, 128, Xq);
+        }
+    return 0;
+}
+
+/* 128x128 weight quantization with UE8M0 scales: sW is uint8 [K/128, N/128]. */
+int oracle_quantize_weight_128x128_ue8m0(const uint16_t *W, uint8_t *Wq, uint8_t *sW,
+                                         int64_t K, int64_t N, int64_t kb0, int64_t kb1)
+{
+    if (K < 0 || N < 0 || K % 128 != 0 || N % 128 != 0 || kb0 < 0 || kb1 > K / 128 || kb0 > kb1)
+        return -1;
+    int64_t NB = N / 128;
+    static __thread int64_t idx[128 * 128];
+    for (int64_t kb = kb0; kb < kb1; ++kb)
+        for (int64_t nb = 0; nb < NB; ++nb) {
+            int64_t t = 0;
+            for (int64_t r = 0; r < 128; ++r)
+                for (int64_t c = 0; c < 128; ++c)
+                    idx[t++] = (kb * 128 + r) * N + nb * 128 + c;
+            sW[kb * NB + nb] = quantize_group_ue8m0(W, idx, 128 * 128, Wq);
+        }
+    return 0;
+}
+
 /* Element-wise encode of n fp32 values (a loop over oracle_e4m3_encode). */
 void oracle_e4m3_encode_array(const float *y, uint8_t *q, int64_t n)
 {
