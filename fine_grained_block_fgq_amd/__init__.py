@@ -16,7 +16,9 @@ import torch
 __all__ = [
     "FgqError", "library_path", "load", "fgq_quantize_act_1x128",
     "fgq_quantize_weight_128x128", "fgq_gemm_fp8_blockscaled",
-    "fgq_gemm_fp8_blockscaled_variant", "fgq_gemm_fp8_blockscaled_quant", "FGQ_OUT_F32", "FGQ_OUT_BF16", "FGQ_GEMM_AUTO",
+    "fgq_gemm_fp8_blockscaled_variant", "fgq_gemm_fp8_blockscaled_quant",
+    "fgq_quantize_act_1x128_ue8m0", "fgq_quantize_weight_128x128_ue8m0",
+    "fgq_gemm_fp8_blockscaled_ue8m0", "FGQ_OUT_F32", "FGQ_OUT_BF16", "FGQ_GEMM_AUTO",
     "FGQ_GEMM_WIDE_256x128", "FGQ_GEMM_WIDE_128x128", "FGQ_GEMM_NARROW_64x32",
 ]
 
@@ -54,6 +56,12 @@ def load() -> ctypes.CDLL:
     lib.fgq_gemm_fp8_blockscaled.argtypes = [p, p, p, p, p, i64, i64, i64, i32, p]
     lib.fgq_gemm_fp8_blockscaled_variant.restype = i32
     lib.fgq_gemm_fp8_blockscaled_variant.argtypes = [p, p, p, p, p, i64, i64, i64, i32, i32, p]
+    lib.fgq_quantize_act_1x128_ue8m0.restype = i32
+    lib.fgq_quantize_act_1x128_ue8m0.argtypes = [p, p, p, i64, i64, p]
+    lib.fgq_quantize_weight_128x128_ue8m0.restype = i32
+    lib.fgq_quantize_weight_128x128_ue8m0.argtypes = [p, p, p, i64, i64, p]
+    lib.fgq_gemm_fp8_blockscaled_ue8m0.restype = i32
+    lib.fgq_gemm_fp8_blockscaled_ue8m0.argtypes = [p, p, p, p, p, i64, i64, i64, i32, i32, p]
     lib.fgq_gemm_fp8_blockscaled_quant.restype = i32
     lib.fgq_gemm_fp8_blockscaled_quant.argtypes = [p, p, p, p, p, p, p, i64, i64, i64, p]
     lib.fgq_status_string.restype = ctypes.c_char_p
@@ -186,3 +194,58 @@ def fgq_gemm_fp8_blockscaled_quant(A_q: torch.Tensor, scale_A: torch.Tensor, B_q
         _dev(C, "C", torch.bfloat16, (M, N)), _dev(C_q, "C_q", _codes_dtype(C_q), (M, N)),
         _dev(scale_C, "scale_C", torch.float32, (M, N // 128)), M, N, K, _stream(stream)))
     return C, C_q, scale_C
+
+
+def fgq_quantize_act_1x128_ue8m0(X: torch.Tensor, Xq: torch.Tensor | None = None,
+                                 scale_X: torch.Tensor | None = None, stream=None):
+    """1x128 activation quantization with UE8M0 exponent-byte scales (uint8 [M, K/128])."""
+    lib = load()
+    M, K = X.shape
+    if Xq is None:
+        Xq = torch.empty((M, K), dtype=torch.uint8, device=X.device)
+    if scale_X is None:
+        scale_X = torch.empty((M, K // 128), dtype=torch.uint8, device=X.device)
+    _check("fgq_quantize_act_1x128_ue8m0", lib.fgq_quantize_act_1x128_ue8m0(
+        _dev(X, "X", torch.bfloat16, (M, K)), _dev(Xq, "Xq", _codes_dtype(Xq), (M, K)),
+        _dev(scale_X, "scale_X", torch.uint8, (M, K // 128)), M, K, _stream(stream)))
+    return Xq, scale_X
+
+
+def fgq_quantize_weight_128x128_ue8m0(W: torch.Tensor, Wq: torch.Tensor | None = None,
+                                      scale_W: torch.Tensor | None = None, stream=None):
+    """128x128 weight quantization with UE8M0 exponent-byte scales (uint8 [K/128, N/128])."""
+    lib = load()
+    K, N = W.shape
+    if Wq is None:
+        Wq = torch.empty((K, N), dtype=torch.uint8, device=W.device)
+    if scale_W is None:
+        scale_W = torch.empty((K // 128, N // 128), dtype=torch.uint8, device=W.device)
+    _check("fgq_quantize_weight_128x128_ue8m0", lib.fgq_quantize_weight_128x128_ue8m0(
+        _dev(W, "W", torch.bfloat16, (K, N)), _dev(Wq, "Wq", _codes_dtype(Wq), (K, N)),
+        _dev(scale_W, "scale_W", torch.uint8, (K // 128, N // 128)), K, N, _stream(stream)))
+    return Wq, scale_W
+
+
+def fgq_gemm_fp8_blockscaled_ue8m0(A_q: torch.Tensor, scale_A: torch.Tensor,
+                                   B_q: torch.Tensor, scale_B: torch.Tensor,
+                                   C: torch.Tensor | None = None,
+                                   out_dtype: torch.dtype = torch.bfloat16,
+                                   variant: int = FGQ_GEMM_AUTO, stream=None):
+    """Block-scaled FP8 GEMM on UE8M0 exponent-byte scales."""
+    lib = load()
+    M, K = A_q.shape
+    K2, N = B_q.shape
+    if K2 != K:
+        raise ValueError(f"A_q is [{M},{K}] but B_q is [{K2},{N}]")
+    if C is None:
+        C = torch.empty((M, N), dtype=out_dtype, device=A_q.device)
+    code = {torch.float32: FGQ_OUT_F32, torch.bfloat16: FGQ_OUT_BF16}.get(C.dtype)
+    if code is None:
+        raise TypeError(f"C must be float32 or bfloat16, got {C.dtype}")
+    _check("fgq_gemm_fp8_blockscaled_ue8m0", lib.fgq_gemm_fp8_blockscaled_ue8m0(
+        _dev(A_q, "A_q", _codes_dtype(A_q), (M, K)),
+        _dev(scale_A, "scale_A", torch.uint8, (M, K // 128)),
+        _dev(B_q, "B_q", _codes_dtype(B_q), (K, N)),
+        _dev(scale_B, "scale_B", torch.uint8, (K // 128, N // 128)),
+        _dev(C, "C", C.dtype, (M, N)), M, N, K, code, int(variant), _stream(stream)))
+    return C

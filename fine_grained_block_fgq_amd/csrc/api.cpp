@@ -22,6 +22,72 @@ bool overlap(const void* a, int64_t na, const void* b, int64_t nb)
 
 int launch_status(hipError_t e) { return e == hipSuccess ? FGQ_OK : FGQ_ERR_LAUNCH; }
 
+// argument checks shared by the fp32-scale and UE8M0-scale entry points (ss: bytes per
+// scale); FGQ_OK for a valid call, including an empty one
+int check_act(const void* X, const void* Xq, const void* sX, int64_t M, int64_t K, int ss)
+{
+    if (M < 0 || K < 0 || K % 128 != 0 || M > kMaxDim || K > kMaxDim)
+        return FGQ_ERR_SHAPE;
+    if (M > 0 && K > 0 && M > ((int64_t(1) << 38) / K))
+        return FGQ_ERR_SHAPE;
+    if (M == 0 || K == 0)
+        return FGQ_OK;
+    if (!X || !Xq || !sX)
+        return FGQ_ERR_NULL;
+    if (misaligned(X) || misaligned(Xq) || misaligned(sX))
+        return FGQ_ERR_ALIGN;
+    const int64_t nx = 2 * M * K, nq = M * K, ns = ss * M * (K / 128);
+    if (overlap(X, nx, Xq, nq) || overlap(X, nx, sX, ns) || overlap(Xq, nq, sX, ns))
+        return FGQ_ERR_ALIAS;
+    return FGQ_OK;
+}
+
+int check_weight(const void* W, const void* Wq, const void* sW, int64_t K, int64_t N, int ss)
+{
+    if (K < 0 || N < 0 || K % 128 != 0 || N % 128 != 0 || K / 128 >= 65536 || N > kMaxDim)
+        return FGQ_ERR_SHAPE;
+    if (K == 0 || N == 0)
+        return FGQ_OK;
+    if (!W || !Wq || !sW)
+        return FGQ_ERR_NULL;
+    if (misaligned(W) || misaligned(Wq) || misaligned(sW))
+        return FGQ_ERR_ALIGN;
+    const int64_t nw = 2 * K * N, nq = K * N, ns = ss * (K / 128) * (N / 128);
+    if (overlap(W, nw, Wq, nq) || overlap(W, nw, sW, ns) || overlap(Wq, nq, sW, ns))
+        return FGQ_ERR_ALIAS;
+    return FGQ_OK;
+}
+
+int check_gemm(const void* A_q, const void* scale_A, const void* B_q, const void* scale_B,
+               const void* C, int64_t M, int64_t N, int64_t K, int out_dtype, int variant,
+               int ss)
+{
+    if (out_dtype != FGQ_OUT_F32 && out_dtype != FGQ_OUT_BF16)
+        return FGQ_ERR_DTYPE;
+    if (variant < FGQ_GEMM_AUTO || variant > FGQ_GEMM_NARROW_64x32)
+        return FGQ_ERR_VARIANT;
+    if (M < 0 || N < 0 || K < 0 || K % 128 != 0 || N % 128 != 0 || M > kMaxDim ||
+        N > kMaxDim || K > kMaxDim)
+        return FGQ_ERR_SHAPE;
+    if (((M + 127) / 128) * (N / 128) > kMaxDim)
+        return FGQ_ERR_SHAPE;
+    if (variant == FGQ_GEMM_NARROW_64x32 && ((M + 63) / 64) * (N / 32) > kMaxDim)
+        return FGQ_ERR_SHAPE;
+    if (M == 0 || N == 0)
+        return FGQ_OK;
+    if (!C || (K > 0 && (!A_q || !scale_A || !B_q || !scale_B)))
+        return FGQ_ERR_NULL;
+    if (misaligned(C) || (K > 0 && (misaligned(A_q) || misaligned(scale_A) ||
+                                    misaligned(B_q) || misaligned(scale_B))))
+        return FGQ_ERR_ALIGN;
+    const int64_t nc = M * N * (out_dtype == FGQ_OUT_BF16 ? 2 : 4);
+    if (K > 0 && (overlap(C, nc, A_q, M * K) || overlap(C, nc, B_q, K * N) ||
+                  overlap(C, nc, scale_A, ss * M * (K / 128)) ||
+                  overlap(C, nc, scale_B, ss * (K / 128) * (N / 128))))
+        return FGQ_ERR_ALIAS;
+    return FGQ_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -46,71 +112,65 @@ const char* fgq_status_string(int status)
 int fgq_quantize_act_1x128(const void* X, void* Xq, float* scale_X, int64_t M, int64_t K,
                            void* stream)
 {
-    if (M < 0 || K < 0 || K % 128 != 0 || M > kMaxDim || K > kMaxDim)
-        return FGQ_ERR_SHAPE;
-    if (M > 0 && K > 0 && M > ((int64_t(1) << 38) / K))
-        return FGQ_ERR_SHAPE;
-    if (M == 0 || K == 0)
-        return FGQ_OK;
-    if (!X || !Xq || !scale_X)
-        return FGQ_ERR_NULL;
-    if (misaligned(X) || misaligned(Xq) || misaligned(scale_X))
-        return FGQ_ERR_ALIGN;
-    const int64_t nx = 2 * M * K, nq = M * K, ns = 4 * M * (K / 128);
-    if (overlap(X, nx, Xq, nq) || overlap(X, nx, scale_X, ns) || overlap(Xq, nq, scale_X, ns))
-        return FGQ_ERR_ALIAS;
+    const int st = check_act(X, Xq, scale_X, M, K, 4);
+    if (st != FGQ_OK || M == 0 || K == 0)
+        return st;
     return launch_status(fgq::launch_quant_act_1x128(X, Xq, scale_X, M, K,
                                                      static_cast<hipStream_t>(stream)));
+}
+
+int fgq_quantize_act_1x128_ue8m0(const void* X, void* Xq, uint8_t* scale_X, int64_t M,
+                                 int64_t K, void* stream)
+{
+    const int st = check_act(X, Xq, scale_X, M, K, 1);
+    if (st != FGQ_OK || M == 0 || K == 0)
+        return st;
+    return launch_status(fgq::launch_quant_act_1x128_ue8m0(X, Xq, scale_X, M, K,
+                                                           static_cast<hipStream_t>(stream)));
 }
 
 int fgq_quantize_weight_128x128(const void* W, void* Wq, float* scale_W, int64_t K,
                                 int64_t N, void* stream)
 {
-    if (K < 0 || N < 0 || K % 128 != 0 || N % 128 != 0 || K / 128 >= 65536 || N > kMaxDim)
-        return FGQ_ERR_SHAPE;
-    if (K == 0 || N == 0)
-        return FGQ_OK;
-    if (!W || !Wq || !scale_W)
-        return FGQ_ERR_NULL;
-    if (misaligned(W) || misaligned(Wq) || misaligned(scale_W))
-        return FGQ_ERR_ALIGN;
-    const int64_t nw = 2 * K * N, nq = K * N, ns = 4 * (K / 128) * (N / 128);
-    if (overlap(W, nw, Wq, nq) || overlap(W, nw, scale_W, ns) || overlap(Wq, nq, scale_W, ns))
-        return FGQ_ERR_ALIAS;
+    const int st = check_weight(W, Wq, scale_W, K, N, 4);
+    if (st != FGQ_OK || K == 0 || N == 0)
+        return st;
     return launch_status(fgq::launch_quant_weight_128x128(W, Wq, scale_W, K, N,
                                                           static_cast<hipStream_t>(stream)));
+}
+
+int fgq_quantize_weight_128x128_ue8m0(const void* W, void* Wq, uint8_t* scale_W, int64_t K,
+                                      int64_t N, void* stream)
+{
+    const int st = check_weight(W, Wq, scale_W, K, N, 1);
+    if (st != FGQ_OK || K == 0 || N == 0)
+        return st;
+    return launch_status(fgq::launch_quant_weight_128x128_ue8m0(
+        W, Wq, scale_W, K, N, static_cast<hipStream_t>(stream)));
 }
 
 int fgq_gemm_fp8_blockscaled_variant(const void* A_q, const float* scale_A, const void* B_q,
                                      const float* scale_B, void* C, int64_t M, int64_t N,
                                      int64_t K, int out_dtype, int variant, void* stream)
 {
-    if (out_dtype != FGQ_OUT_F32 && out_dtype != FGQ_OUT_BF16)
-        return FGQ_ERR_DTYPE;
-    if (variant < FGQ_GEMM_AUTO || variant > FGQ_GEMM_NARROW_64x32)
-        return FGQ_ERR_VARIANT;
-    if (M < 0 || N < 0 || K < 0 || K % 128 != 0 || N % 128 != 0 || M > kMaxDim ||
-        N > kMaxDim || K > kMaxDim)
-        return FGQ_ERR_SHAPE;
-    if (((M + 127) / 128) * (N / 128) > kMaxDim)
-        return FGQ_ERR_SHAPE;
-    if (variant == FGQ_GEMM_NARROW_64x32 && ((M + 63) / 64) * (N / 32) > kMaxDim)
-        return FGQ_ERR_SHAPE;
-    if (M == 0 || N == 0)
-        return FGQ_OK;
-    if (!C || (K > 0 && (!A_q || !scale_A || !B_q || !scale_B)))
-        return FGQ_ERR_NULL;
-    if (misaligned(C) || (K > 0 && (misaligned(A_q) || misaligned(scale_A) ||
-                                    misaligned(B_q) || misaligned(scale_B))))
-        return FGQ_ERR_ALIGN;
-    const int64_t nc = M * N * (out_dtype == FGQ_OUT_BF16 ? 2 : 4);
-    if (K > 0 && (overlap(C, nc, A_q, M * K) || overlap(C, nc, B_q, K * N) ||
-                  overlap(C, nc, scale_A, 4 * M * (K / 128)) ||
-                  overlap(C, nc, scale_B, 4 * (K / 128) * (N / 128))))
-        return FGQ_ERR_ALIAS;
+    const int st = check_gemm(A_q, scale_A, B_q, scale_B, C, M, N, K, out_dtype, variant, 4);
+    if (st != FGQ_OK || M == 0 || N == 0)
+        return st;
     return launch_status(fgq::launch_gemm_fp8_blockscaled(A_q, scale_A, B_q, scale_B, C, M, N, K,
                                                           out_dtype == FGQ_OUT_BF16, variant,
                                                           static_cast<hipStream_t>(stream)));
+}
+
+int fgq_gemm_fp8_blockscaled_ue8m0(const void* A_q, const uint8_t* scale_A, const void* B_q,
+                                   const uint8_t* scale_B, void* C, int64_t M, int64_t N,
+                                   int64_t K, int out_dtype, int variant, void* stream)
+{
+    const int st = check_gemm(A_q, scale_A, B_q, scale_B, C, M, N, K, out_dtype, variant, 1);
+    if (st != FGQ_OK || M == 0 || N == 0)
+        return st;
+    return launch_status(fgq::launch_gemm_fp8_blockscaled_ue8m0(
+        A_q, scale_A, B_q, scale_B, C, M, N, K, out_dtype == FGQ_OUT_BF16, variant,
+        static_cast<hipStream_t>(stream)));
 }
 
 int fgq_gemm_fp8_blockscaled(const void* A_q, const float* scale_A, const void* B_q,

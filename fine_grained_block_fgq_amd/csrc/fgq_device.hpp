@@ -141,4 +141,66 @@ __device__ __forceinline__ u32x2 quantize8(u32x4 v, const GroupScale& g)
     return q;
 }
 
+// ---------------------------------------------------------------------------------------
+// UE8M0 (power-of-two) group scales: the stored byte e stands for s = 2^(e-127) (page
+// "Fine-Grained FP8/FP4 Quantization", section "Blackwell: Native Block Scaling"); e is the
+// smallest exponent with 448*s >= amax, so no code saturates.  With amax = 1.f * 2^E in
+// bf16 (E from the exponent field, f from the 7 mantissa bits): 448 = 1.75 * 2^8, so
+// 448 * 2^(E-8) covers amax exactly when f <= 1.75 (mantissa bits <= 0x60), otherwise one
+// more power of two is needed; e = E - 8 (+1) + 127, clamped at 0 for amax below 448*2^-127
+// (tiny and all-zero groups).  The quotient x/s is x * 2^(127-e): a product with an exact
+// power of two, so it is the correctly rounded quotient itself.
+// ---------------------------------------------------------------------------------------
+struct Pow2Scale {
+    uint32_t e;   // stored exponent byte
+    float r;      // 1/s = 2^(127-e), a normal float for every e this rule gives (0..247)
+};
+
+__device__ __forceinline__ Pow2Scale pow2_scale(uint32_t amax_bits16)
+{
+    const int ef = (int)((amax_bits16 >> 7) & 0xFF);
+    int e = ef - 8 + ((amax_bits16 & 0x7F) > 0x60 ? 1 : 0);
+    e = e < 0 ? 0 : e;
+    Pow2Scale p;
+    p.e = (uint32_t)e;
+    p.r = __uint_as_float((uint32_t)(254 - e) << 23);
+    return p;
+}
+
+// quantize 8 bf16 values with a power-of-two scale
+__device__ __forceinline__ u32x2 quantize8_pow2(u32x4 v, const Pow2Scale& p)
+{
+    uint32_t w[4] = {v.x, v.y, v.z, v.w};
+    uint32_t out[2];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+        const float y0 = __uint_as_float(w[2 * h] << 16) * p.r;
+        const float y1 = __uint_as_float(w[2 * h] & 0xFFFF0000u) * p.r;
+        const float y2 = __uint_as_float(w[2 * h + 1] << 16) * p.r;
+        const float y3 = __uint_as_float(w[2 * h + 1] & 0xFFFF0000u) * p.r;
+        int packed = __builtin_amdgcn_cvt_pk_fp8_f32(y0, y1, 0, false);
+        packed = __builtin_amdgcn_cvt_pk_fp8_f32(y2, y3, packed, true);
+        out[h] = (uint32_t)packed;
+    }
+    return u32x2{out[0], out[1]};
+}
+
+// Scale policies for the quantization kernels: fp32 scale amax/448, or UE8M0 exponent
+struct ScaleF32 {
+    typedef float stored_t;
+    GroupScale g;
+    __device__ __forceinline__ explicit ScaleF32(uint32_t amax_bits16)
+        : g(group_scale(amax_bits16)) {}
+    __device__ __forceinline__ u32x2 quant(u32x4 v) const { return quantize8(v, g); }
+    __device__ __forceinline__ float stored() const { return g.s; }
+};
+struct ScaleUE8M0 {
+    typedef uint8_t stored_t;
+    Pow2Scale p;
+    __device__ __forceinline__ explicit ScaleUE8M0(uint32_t amax_bits16)
+        : p(pow2_scale(amax_bits16)) {}
+    __device__ __forceinline__ u32x2 quant(u32x4 v) const { return quantize8_pow2(v, p); }
+    __device__ __forceinline__ uint8_t stored() const { return (uint8_t)p.e; }
+};
+
 }  // namespace fgq

@@ -9,6 +9,11 @@ hipError_t launch_quant_act_1x128(const void* X, void* Xq, float* sX, int64_t M,
                                   hipStream_t stream);
 hipError_t launch_quant_weight_128x128(const void* W, void* Wq, float* sW, int64_t K,
                                        int64_t N, hipStream_t stream);
+// the same with UE8M0 (exponent byte) scales
+hipError_t launch_quant_act_1x128_ue8m0(const void* X, void* Xq, uint8_t* sX, int64_t M,
+                                        int64_t K, hipStream_t stream);
+hipError_t launch_quant_weight_128x128_ue8m0(const void* W, void* Wq, uint8_t* sW, int64_t K,
+                                             int64_t N, hipStream_t stream);
 // GEMM kernel families (values of fgq_gemm_variant)
 enum GemmVariant { GEMM_AUTO = 0, GEMM_WIDE_256x128 = 1, GEMM_WIDE_128x128 = 2, GEMM_NARROW = 3 };
 
@@ -17,6 +22,12 @@ hipError_t launch_gemm_fp8_blockscaled(const void* A_q, const float* sA, const v
                                        const float* sB, void* C, int64_t M, int64_t N,
                                        int64_t K, int out_bf16, int variant,
                                        hipStream_t stream);
+
+// the same GEMM with UE8M0 exponent-byte scales (2^(e-127))
+hipError_t launch_gemm_fp8_blockscaled_ue8m0(const void* A_q, const uint8_t* sA,
+                                             const void* B_q, const uint8_t* sB, void* C,
+                                             int64_t M, int64_t N, int64_t K, int out_bf16,
+                                             int variant, hipStream_t stream);
 
 // C = bf16 GEMM result, plus its 1x128 E4M3 quantization (Cq [M,N], sC [M,N/128])
 hipError_t launch_gemm_fp8_blockscaled_quant(const void* A_q, const float* sA, const void* B_q,

@@ -146,14 +146,56 @@ __device__ __forceinline__ void dma_b32(const void* gptr, uint32_t lds)
                  : "memory", "m0");
 }
 
+// one byte per lane, zero-extended into the lane's dword slot [lds + 4*lane]
+__device__ __forceinline__ void dma_u8(const void* gptr, uint32_t lds)
+{
+    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_ubyte %0, off"
+                 :
+                 : "v"(gptr), "s"(lds)
+                 : "memory", "m0");
+}
+
+// Scale formats the GEMM reads: fp32 scales, or UE8M0 exponent bytes e standing for
+// 2^(e-127) (page "Fine-Grained FP8/FP4 Quantization", section "Blackwell: Native Block
+// Scaling").  Either way one 4-byte LDS slot per tile row carries scale_A of the chunk, and
+// the combined scale of a row is formed in fp32: sA*sB, or 2^(eA-127) * 2^(eB-127) by an
+// exponent add (exact unless it falls below the fp32 range).
+template <bool E8>
+struct ScaleIn;
+template <>
+struct ScaleIn<false> {
+    typedef float T;
+    static __device__ __forceinline__ void dma(const T* p, uint32_t lds) { dma_b32(p, lds); }
+    static __device__ __forceinline__ float value(T v) { return v; }
+    static __device__ __forceinline__ f32x4 combine(const uint8_t LDS* p, float sb)
+    {
+        return *(const f32x4 LDS*)p * sb;
+    }
+};
+template <>
+struct ScaleIn<true> {
+    typedef uint8_t T;
+    static __device__ __forceinline__ void dma(const T* p, uint32_t lds) { dma_u8(p, lds); }
+    static __device__ __forceinline__ float value(T e)
+    {
+        return __builtin_ldexpf(1.0f, (int)e - 127);
+    }
+    static __device__ __forceinline__ f32x4 combine(const uint8_t LDS* p, float sb)
+    {
+        const i32x4 e = *(const i32x4 LDS*)p;
+        return f32x4{__builtin_ldexpf(sb, e[0] - 127), __builtin_ldexpf(sb, e[1] - 127),
+                     __builtin_ldexpf(sb, e[2] - 127), __builtin_ldexpf(sb, e[3] - 127)};
+    }
+};
+
 __device__ __forceinline__ uint32_t lds_addr(const uint8_t LDS* p)
 {
     return (uint32_t)(uintptr_t)p;
 }
 
-template <class Cfg>
+template <class Cfg, class SI>
 __device__ __forceinline__ void load_stage(uint8_t LDS* stage, const uint8_t* __restrict__ A,
-                                           const float* __restrict__ sA,
+                                           const typename SI::T* __restrict__ sA,
                                            const uint8_t* __restrict__ B, int64_t M,
                                            int64_t N, int64_t K, int64_t m0, int64_t n0,
                                            int64_t kb, int wave, int lane)
@@ -186,13 +228,13 @@ __device__ __forceinline__ void load_stage(uint8_t LDS* stage, const uint8_t* __
     if (wave < Cfg::S_LOADS) {
         int64_t gm = m0 + wave * 64 + lane;
         gm = gm < M ? gm : M - 1;
-        dma_b32(sA + gm * KB + kb, lds_addr(stage + Cfg::A_BYTES + Cfg::B_BYTES + wave * 256));
+        SI::dma(sA + gm * KB + kb, lds_addr(stage + Cfg::A_BYTES + Cfg::B_BYTES + wave * 256));
     }
 }
 
 // One 128-K chunk of the wave's 16x16 tiles: f16 operands, four chained f16 MFMAs per
 // tile, then acc += P * (sA*sB).
-template <class Cfg>
+template <class Cfg, class SI>
 __device__ __forceinline__ void compute_chunk(const uint8_t LDS* cur, const int (&a_off)[Cfg::FM][2],
                                               const int (&b_off)[Cfg::FN][4], int s_off, float sb,
                                               f32x4 (&acc)[Cfg::FM][Cfg::FN])
@@ -201,8 +243,7 @@ __device__ __forceinline__ void compute_chunk(const uint8_t LDS* cur, const int 
     f32x4 cs[Cfg::FM];
 #pragma unroll
     for (int i = 0; i < Cfg::FM; ++i) {
-        const f32x4 sa = *(const f32x4 LDS*)(cur + s_off + i * 64);
-        cs[i] = sa * sb;
+        cs[i] = SI::combine(cur + s_off + i * 64, sb);
     }
     // A operands: lane bytes 8t..8t+7 of its 32 (k = 32g + 8t + b) -> sub-step t
     i32x4 araw[Cfg::FM][2];
@@ -312,10 +353,11 @@ __device__ __forceinline__ void store_quant_tile(uint8_t LDS* smem,
     }
 }
 
-template <class Cfg, bool OUT_BF16, bool FUSE = false>
+template <class Cfg, class SI, bool OUT_BF16, bool FUSE = false>
 __global__ __launch_bounds__(Cfg::NT) void gemm_fp8_blockscaled_kernel(
-    const uint8_t* __restrict__ A, const float* __restrict__ sA, const uint8_t* __restrict__ B,
-    const float* __restrict__ sB, void* __restrict__ Cout, int64_t M, int64_t N, int64_t K,
+    const uint8_t* __restrict__ A, const typename SI::T* __restrict__ sA,
+    const uint8_t* __restrict__ B, const typename SI::T* __restrict__ sB,
+    void* __restrict__ Cout, int64_t M, int64_t N, int64_t K,
     uint8_t* __restrict__ Cq = nullptr, float* __restrict__ sC = nullptr)
 {
     __shared__ __attribute__((aligned(1024))) uint8_t smem_raw[Cfg::STAGES * Cfg::STAGE];
@@ -378,12 +420,12 @@ __global__ __launch_bounds__(Cfg::NT) void gemm_fp8_blockscaled_kernel(
 #pragma unroll
     for (int st = 0; st < Cfg::STAGES - 1; ++st)
         if (st < KB)
-            load_stage<Cfg>(smem + st * Cfg::STAGE, A, sA, B, M, N, K, m0, n0, st, wave, lane);
+            load_stage<Cfg, SI>(smem + st * Cfg::STAGE, A, sA, B, M, N, K, m0, n0, st, wave, lane);
 
     // scale_B of the wave's column block, loaded one chunk ahead: the scalar load then
     // completes under the LDS barrier's wait instead of stalling the chunk's LDS reads
-    const float* const sB_col = sB + (nb_wave < NB ? nb_wave : NB - 1);
-    float sb_next = KB > 0 ? sB_col[0] : 0.0f;
+    const typename SI::T* const sB_col = sB + (nb_wave < NB ? nb_wave : NB - 1);
+    float sb_next = KB > 0 ? SI::value(sB_col[0]) : 0.0f;
     for (int64_t kb = 0; kb < KB; ++kb) {
         const uint8_t LDS* cur = smem + (kb % Cfg::STAGES) * Cfg::STAGE;
         // chunk kb has landed once only the later chunks' loads may still be outstanding
@@ -396,11 +438,11 @@ __global__ __launch_bounds__(Cfg::NT) void gemm_fp8_blockscaled_kernel(
         const float sb = sb_next;
         const int64_t nxt = kb + Cfg::STAGES - 1;
         if (nxt < KB)
-            load_stage<Cfg>(smem + (nxt % Cfg::STAGES) * Cfg::STAGE, A, sA, B, M, N, K, m0, n0,
+            load_stage<Cfg, SI>(smem + (nxt % Cfg::STAGES) * Cfg::STAGE, A, sA, B, M, N, K, m0, n0,
                             nxt, wave, lane);
         if (kb + 1 < KB)
-            sb_next = sB_col[(kb + 1) * NB];
-        compute_chunk<Cfg>(cur, a_off, b_off, s_off, sb, acc);
+            sb_next = SI::value(sB_col[(kb + 1) * NB]);
+        compute_chunk<Cfg, SI>(cur, a_off, b_off, s_off, sb, acc);
         if (Cfg::STAGES == 2)
             lds_barrier();   // chunk kb fully read before the next iteration refills it
     }
@@ -436,18 +478,20 @@ __global__ __launch_bounds__(Cfg::NT) void gemm_fp8_blockscaled_kernel(
     }
 }
 
-template <class Cfg>
-static hipError_t launch_cfg(const void* A_q, const float* sA, const void* B_q, const float* sB,
+template <class Cfg, class SI>
+static hipError_t launch_cfg(const void* A_q, const void* sA_, const void* B_q, const void* sB_,
                              void* C, int64_t M, int64_t N, int64_t K, int out_bf16,
                              hipStream_t stream)
 {
+    const typename SI::T* sA = static_cast<const typename SI::T*>(sA_);
+    const typename SI::T* sB = static_cast<const typename SI::T*>(sB_);
     const int64_t tiles = ((M + Cfg::BM - 1) / Cfg::BM) * ((N + Cfg::BN - 1) / Cfg::BN);
     if (out_bf16)
-        hipLaunchKernelGGL((gemm_fp8_blockscaled_kernel<Cfg, true>), dim3((unsigned)tiles),
+        hipLaunchKernelGGL((gemm_fp8_blockscaled_kernel<Cfg, SI, true>), dim3((unsigned)tiles),
                            dim3(Cfg::NT), 0, stream, static_cast<const uint8_t*>(A_q), sA,
                            static_cast<const uint8_t*>(B_q), sB, C, M, N, K);
     else
-        hipLaunchKernelGGL((gemm_fp8_blockscaled_kernel<Cfg, false>), dim3((unsigned)tiles),
+        hipLaunchKernelGGL((gemm_fp8_blockscaled_kernel<Cfg, SI, false>), dim3((unsigned)tiles),
                            dim3(Cfg::NT), 0, stream, static_cast<const uint8_t*>(A_q), sA,
                            static_cast<const uint8_t*>(B_q), sB, C, M, N, K);
     return hipGetLastError();
@@ -487,9 +531,9 @@ struct NarrowCfg {
 
 // one wave fills its stage with chunk kb: A rows m0..m0+BM-1, B rows of the chunk for
 // columns n0..n0+31, and scale_A of the rows
-template <class Cfg>
+template <class Cfg, class SI>
 __device__ __forceinline__ void narrow_load(uint8_t LDS* stage, const uint8_t* __restrict__ A,
-                                            const float* __restrict__ sA,
+                                            const typename SI::T* __restrict__ sA,
                                             const uint8_t* __restrict__ B, int64_t M, int64_t N,
                                             int64_t K, int64_t m0, int64_t n0, int64_t kb,
                                             int lane)
@@ -511,13 +555,14 @@ __device__ __forceinline__ void narrow_load(uint8_t LDS* stage, const uint8_t* _
     }
     int64_t gm = m0 + lane;
     gm = gm < M ? gm : M - 1;
-    dma_b32(sA + gm * (K / 128) + kb, lds_addr(stage + Cfg::A_BYTES + Cfg::B_BYTES));
+    SI::dma(sA + gm * (K / 128) + kb, lds_addr(stage + Cfg::A_BYTES + Cfg::B_BYTES));
 }
 
-template <class Cfg, bool OUT_BF16>
+template <class Cfg, class SI, bool OUT_BF16>
 __global__ __launch_bounds__(Cfg::NT) void gemm_fp8_blockscaled_narrow_kernel(
-    const uint8_t* __restrict__ A, const float* __restrict__ sA, const uint8_t* __restrict__ B,
-    const float* __restrict__ sB, void* __restrict__ Cout, int64_t M, int64_t N, int64_t K)
+    const uint8_t* __restrict__ A, const typename SI::T* __restrict__ sA,
+    const uint8_t* __restrict__ B, const typename SI::T* __restrict__ sB,
+    void* __restrict__ Cout, int64_t M, int64_t N, int64_t K)
 {
     __shared__ __attribute__((aligned(1024))) uint8_t smem_raw[Cfg::LDS_BYTES];
     uint8_t LDS* const smem = (uint8_t LDS*)smem_raw;
@@ -567,7 +612,7 @@ __global__ __launch_bounds__(Cfg::NT) void gemm_fp8_blockscaled_narrow_kernel(
 #pragma unroll
     for (int st = 0; st < Cfg::STAGES - 1; ++st)
         if (st < nc)
-            narrow_load<Cfg>(ring + st * Cfg::STAGE, A, sA, B, M, N, K, m0, n0,
+            narrow_load<Cfg, SI>(ring + st * Cfg::STAGE, A, sA, B, M, N, K, m0, n0,
                              wave + st * Cfg::KW, lane);
     for (int64_t c = 0; c < nc; ++c) {
         // chunk c has landed once only the next chunk's loads may be outstanding; every
@@ -580,11 +625,11 @@ __global__ __launch_bounds__(Cfg::NT) void gemm_fp8_blockscaled_narrow_kernel(
         asm volatile("" ::: "memory");
         const int64_t nxt = c + Cfg::STAGES - 1;
         if (nxt < nc)
-            narrow_load<Cfg>(ring + (nxt % Cfg::STAGES) * Cfg::STAGE, A, sA, B, M, N, K, m0,
+            narrow_load<Cfg, SI>(ring + (nxt % Cfg::STAGES) * Cfg::STAGE, A, sA, B, M, N, K, m0,
                              n0, wave + nxt * Cfg::KW, lane);
         const int64_t kb = wave + c * Cfg::KW;
-        const float sb = sB[kb * NB + nb];
-        compute_chunk<Cfg>(ring + (c % Cfg::STAGES) * Cfg::STAGE, a_off, b_off, s_off, sb, acc);
+        const float sb = SI::value(sB[kb * NB + nb]);
+        compute_chunk<Cfg, SI>(ring + (c % Cfg::STAGES) * Cfg::STAGE, a_off, b_off, s_off, sb, acc);
     }
 
     // sum the KW partial tiles in wave order, then store coalesced
@@ -617,19 +662,21 @@ __global__ __launch_bounds__(Cfg::NT) void gemm_fp8_blockscaled_narrow_kernel(
     }
 }
 
-template <class Cfg>
-static hipError_t launch_narrow(const void* A_q, const float* sA, const void* B_q,
-                                const float* sB, void* C, int64_t M, int64_t N, int64_t K,
+template <class Cfg, class SI>
+static hipError_t launch_narrow(const void* A_q, const void* sA_, const void* B_q,
+                                const void* sB_, void* C, int64_t M, int64_t N, int64_t K,
                                 int out_bf16, hipStream_t stream)
 {
+    const typename SI::T* sA = static_cast<const typename SI::T*>(sA_);
+    const typename SI::T* sB = static_cast<const typename SI::T*>(sB_);
     const int64_t tiles = ((M + Cfg::BM - 1) / Cfg::BM) * (N / Cfg::BN);
     if (out_bf16)
-        hipLaunchKernelGGL((gemm_fp8_blockscaled_narrow_kernel<Cfg, true>),
+        hipLaunchKernelGGL((gemm_fp8_blockscaled_narrow_kernel<Cfg, SI, true>),
                            dim3((unsigned)tiles), dim3(Cfg::NT), 0, stream,
                            static_cast<const uint8_t*>(A_q), sA,
                            static_cast<const uint8_t*>(B_q), sB, C, M, N, K);
     else
-        hipLaunchKernelGGL((gemm_fp8_blockscaled_narrow_kernel<Cfg, false>),
+        hipLaunchKernelGGL((gemm_fp8_blockscaled_narrow_kernel<Cfg, SI, false>),
                            dim3((unsigned)tiles), dim3(Cfg::NT), 0, stream,
                            static_cast<const uint8_t*>(A_q), sA,
                            static_cast<const uint8_t*>(B_q), sB, C, M, N, K);
@@ -642,7 +689,7 @@ static hipError_t launch_fused(const void* A_q, const float* sA, const void* B_q
                                hipStream_t stream)
 {
     const int64_t tiles = ((M + Cfg::BM - 1) / Cfg::BM) * ((N + Cfg::BN - 1) / Cfg::BN);
-    hipLaunchKernelGGL((gemm_fp8_blockscaled_kernel<Cfg, true, true>), dim3((unsigned)tiles),
+    hipLaunchKernelGGL((gemm_fp8_blockscaled_kernel<Cfg, ScaleIn<false>, true, true>), dim3((unsigned)tiles),
                        dim3(Cfg::NT), 0, stream, static_cast<const uint8_t*>(A_q), sA,
                        static_cast<const uint8_t*>(B_q), sB, C, M, N, K,
                        static_cast<uint8_t*>(Cq), sC);
@@ -662,10 +709,10 @@ using CfgSmall = GemmCfg<FGQ_SMALL_CFG>;
 #endif
 using CfgNarrow = NarrowCfg<FGQ_NARROW_CFG>;
 
-hipError_t launch_gemm_fp8_blockscaled(const void* A_q, const float* sA, const void* B_q,
-                                       const float* sB, void* C, int64_t M, int64_t N,
-                                       int64_t K, int out_bf16, int variant,
-                                       hipStream_t stream)
+template <class SI>
+static hipError_t launch_gemm(const void* A_q, const void* sA, const void* B_q, const void* sB,
+                              void* C, int64_t M, int64_t N, int64_t K, int out_bf16,
+                              int variant, hipStream_t stream)
 {
     if (variant == GEMM_AUTO) {
         // wide tiles while they fill the 256 CUs at least once, else narrow tiles
@@ -677,14 +724,30 @@ hipError_t launch_gemm_fp8_blockscaled(const void* A_q, const float* sA, const v
     }
     switch (variant) {
     case GEMM_WIDE_256x128:
-        return launch_cfg<CfgLarge>(A_q, sA, B_q, sB, C, M, N, K, out_bf16, stream);
+        return launch_cfg<CfgLarge, SI>(A_q, sA, B_q, sB, C, M, N, K, out_bf16, stream);
     case GEMM_WIDE_128x128:
-        return launch_cfg<CfgSmall>(A_q, sA, B_q, sB, C, M, N, K, out_bf16, stream);
+        return launch_cfg<CfgSmall, SI>(A_q, sA, B_q, sB, C, M, N, K, out_bf16, stream);
     case GEMM_NARROW:
-        return launch_narrow<CfgNarrow>(A_q, sA, B_q, sB, C, M, N, K, out_bf16, stream);
+        return launch_narrow<CfgNarrow, SI>(A_q, sA, B_q, sB, C, M, N, K, out_bf16, stream);
     default:
         return hipErrorInvalidValue;
     }
+}
+
+hipError_t launch_gemm_fp8_blockscaled(const void* A_q, const float* sA, const void* B_q,
+                                       const float* sB, void* C, int64_t M, int64_t N,
+                                       int64_t K, int out_bf16, int variant,
+                                       hipStream_t stream)
+{
+    return launch_gemm<ScaleIn<false>>(A_q, sA, B_q, sB, C, M, N, K, out_bf16, variant, stream);
+}
+
+hipError_t launch_gemm_fp8_blockscaled_ue8m0(const void* A_q, const uint8_t* sA,
+                                             const void* B_q, const uint8_t* sB, void* C,
+                                             int64_t M, int64_t N, int64_t K, int out_bf16,
+                                             int variant, hipStream_t stream)
+{
+    return launch_gemm<ScaleIn<true>>(A_q, sA, B_q, sB, C, M, N, K, out_bf16, variant, stream);
 }
 
 hipError_t launch_gemm_fp8_blockscaled_quant(const void* A_q, const float* sA, const void* B_q,

@@ -39,8 +39,10 @@ constexpr int ACT_TILES_PER_BLOCK = ACT_WAVES * ACT_TILES_PER_WAVE;
 // looping over the tile groups with a grid stride)
 constexpr int64_t ACT_GRID = FGQ_ACT_GRID;
 
+template <class Scale>
 __global__ __launch_bounds__(64 * ACT_WAVES) void quant_act_1x128_kernel(
-    const u32x4* __restrict__ X, u32x2* __restrict__ Xq, float* __restrict__ sX, int64_t T)
+    const u32x4* __restrict__ X, u32x2* __restrict__ Xq, typename Scale::stored_t* __restrict__ sX,
+    int64_t T)
 {
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
@@ -59,12 +61,12 @@ __global__ __launch_bounds__(64 * ACT_WAVES) void quant_act_1x128_kernel(
 #pragma unroll
     for (int u = 0; u < ACT_UNROLL; ++u) {
         const int64_t t = t0 + 4 * u;
-        const GroupScale g = group_scale(row16_max(absmax_bits8(v[u])));
-        const u32x2 q = quantize8(v[u], g);
+        const Scale g(row16_max(absmax_bits8(v[u])));
+        const u32x2 q = g.quant(v[u]);
         if (t < T) {
             __builtin_nontemporal_store(q, &Xq[t * 16 + j]);
             if (j == 0)
-                sX[t] = g.s;
+                sX[t] = g.stored();
         }
     }
     }
@@ -80,9 +82,10 @@ __global__ __launch_bounds__(64 * ACT_WAVES) void quant_act_1x128_kernel(
 constexpr int WQ_THREADS = 256;
 constexpr int WQ_CHUNKS = 2048 / WQ_THREADS;
 
+template <class Scale>
 __global__ __launch_bounds__(WQ_THREADS) void quant_weight_128x128_kernel(
-    const uint8_t* __restrict__ W, uint8_t* __restrict__ Wq, float* __restrict__ sW,
-    int64_t N)
+    const uint8_t* __restrict__ W, uint8_t* __restrict__ Wq,
+    typename Scale::stored_t* __restrict__ sW, int64_t N)
 {
     __shared__ uint32_t wave_amax[WQ_THREADS / 64];
     const int tid = threadIdx.x;
@@ -108,37 +111,65 @@ __global__ __launch_bounds__(WQ_THREADS) void quant_weight_128x128_kernel(
         wave_amax[tid >> 6] = m;
     __syncthreads();
     m = max(max(wave_amax[0], wave_amax[1]), max(wave_amax[2], wave_amax[3]));
-    const GroupScale g = group_scale(m);
+    const Scale g(m);
 #pragma unroll
     for (int i = 0; i < WQ_CHUNKS; ++i) {
         const int c = i * WQ_THREADS + tid;
         const int row = c >> 4, col8 = (c & 15) * 8;
-        __builtin_nontemporal_store(quantize8(v[i], g),
+        __builtin_nontemporal_store(g.quant(v[i]),
                                     reinterpret_cast<u32x2*>(qblk + (int64_t)row * N + col8));
     }
     if (tid == 0)
-        sW[kb * NB + nb] = g.s;
+        sW[kb * NB + nb] = g.stored();
 }
 
-hipError_t launch_quant_act_1x128(const void* X, void* Xq, float* sX, int64_t M, int64_t K,
-                                  hipStream_t stream)
+template <class Scale>
+static hipError_t launch_act(const void* X, void* Xq, typename Scale::stored_t* sX, int64_t M,
+                             int64_t K, hipStream_t stream)
 {
     const int64_t T = M * (K / 128);
     int64_t blocks = (T + ACT_TILES_PER_BLOCK - 1) / ACT_TILES_PER_BLOCK;
     if (ACT_GRID > 0 && blocks > ACT_GRID)
         blocks = ACT_GRID;
-    hipLaunchKernelGGL(quant_act_1x128_kernel, dim3((unsigned)blocks), dim3(64 * ACT_WAVES), 0,
-                       stream, static_cast<const u32x4*>(X), static_cast<u32x2*>(Xq), sX, T);
+    hipLaunchKernelGGL(quant_act_1x128_kernel<Scale>, dim3((unsigned)blocks),
+                       dim3(64 * ACT_WAVES), 0, stream, static_cast<const u32x4*>(X),
+                       static_cast<u32x2*>(Xq), sX, T);
     return hipGetLastError();
+}
+
+template <class Scale>
+static hipError_t launch_weight(const void* W, void* Wq, typename Scale::stored_t* sW,
+                                int64_t K, int64_t N, hipStream_t stream)
+{
+    hipLaunchKernelGGL(quant_weight_128x128_kernel<Scale>,
+                       dim3((unsigned)(N / 128), (unsigned)(K / 128)), dim3(WQ_THREADS), 0,
+                       stream, static_cast<const uint8_t*>(W), static_cast<uint8_t*>(Wq), sW,
+                       N);
+    return hipGetLastError();
+}
+
+hipError_t launch_quant_act_1x128(const void* X, void* Xq, float* sX, int64_t M, int64_t K,
+                                  hipStream_t stream)
+{
+    return launch_act<ScaleF32>(X, Xq, sX, M, K, stream);
 }
 
 hipError_t launch_quant_weight_128x128(const void* W, void* Wq, float* sW, int64_t K,
                                        int64_t N, hipStream_t stream)
 {
-    hipLaunchKernelGGL(quant_weight_128x128_kernel, dim3((unsigned)(N / 128), (unsigned)(K / 128)),
-                       dim3(WQ_THREADS), 0, stream, static_cast<const uint8_t*>(W),
-                       static_cast<uint8_t*>(Wq), sW, N);
-    return hipGetLastError();
+    return launch_weight<ScaleF32>(W, Wq, sW, K, N, stream);
+}
+
+hipError_t launch_quant_act_1x128_ue8m0(const void* X, void* Xq, uint8_t* sX, int64_t M,
+                                        int64_t K, hipStream_t stream)
+{
+    return launch_act<ScaleUE8M0>(X, Xq, sX, M, K, stream);
+}
+
+hipError_t launch_quant_weight_128x128_ue8m0(const void* W, void* Wq, uint8_t* sW, int64_t K,
+                                             int64_t N, hipStream_t stream)
+{
+    return launch_weight<ScaleUE8M0>(W, Wq, sW, K, N, stream);
 }
 
 }  // namespace fgq

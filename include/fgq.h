@@ -132,6 +132,30 @@ int fgq_gemm_fp8_blockscaled_quant(const void* A_q, const float* scale_A, const 
                                    const float* scale_B, void* C, void* C_q, float* scale_C,
                                    int64_t M, int64_t N, int64_t K, void* stream);
 
+/*
+ * UE8M0 (power-of-two) scale variants.  Page "Fine-Grained FP8/FP4 Quantization", section
+ * "Blackwell: Native Block Scaling" and table "UE8M0 vs E4M3 Scale Formats": a scale is one
+ * unsigned exponent byte e standing for 2^(e-127).  Same 1x128 / 128x128 groups, shapes and
+ * code rule as the fp32-scale calls; the scale of a group is the smallest power of two
+ * 2^(e-127), 0 <= e <= 254, with 448 * 2^(e-127) >= amax (e = 0 for groups whose amax is
+ * below 448 * 2^-127, including all-zero groups), so codes never saturate and x / scale is
+ * exact.  Scale arrays are uint8 with the same shapes as the fp32 ones.  Requirements and
+ * errors as the fp32-scale calls.
+ */
+int fgq_quantize_act_1x128_ue8m0(const void* X, void* Xq, uint8_t* scale_X, int64_t M,
+                                 int64_t K, void* stream);
+int fgq_quantize_weight_128x128_ue8m0(const void* W, void* Wq, uint8_t* scale_W, int64_t K,
+                                      int64_t N, void* stream);
+/*
+ * GEMM on UE8M0 scales: C as fgq_gemm_fp8_blockscaled with scale_A[m,kb] = 2^(eA-127) and
+ * scale_B[kb,nb] = 2^(eB-127); the combined scale of a chunk is the exact power of two
+ * 2^(eA+eB-254) (flushed to zero below the fp32 range).  `variant` as in
+ * fgq_gemm_fp8_blockscaled_variant (FGQ_GEMM_AUTO to let the shape decide).
+ */
+int fgq_gemm_fp8_blockscaled_ue8m0(const void* A_q, const uint8_t* scale_A, const void* B_q,
+                                   const uint8_t* scale_B, void* C, int64_t M, int64_t N,
+                                   int64_t K, int out_dtype, int variant, void* stream);
+
 /* Static text for a status code. */
 const char* fgq_status_string(int status);
 

@@ -115,3 +115,21 @@ T1 = 0x60000
 ])
 def test_gemm_quant_validation(args, want):
     assert fgq.load().fgq_gemm_fp8_blockscaled_quant(*args, None) == want
+
+
+@pytest.mark.parametrize("fn,args,want", [
+    ("fgq_quantize_act_1x128_ue8m0", (P, Q, R, 4, 100), -2),
+    ("fgq_quantize_act_1x128_ue8m0", (P, Q, R + 1, 4, 128), -3),
+    ("fgq_quantize_act_1x128_ue8m0", (P, Q, P + 32, 4, 128), -6),
+    ("fgq_quantize_act_1x128_ue8m0", (None, None, None, 0, 128), 0),
+    ("fgq_quantize_weight_128x128_ue8m0", (P, Q, R, 100, 128), -2),
+    ("fgq_quantize_weight_128x128_ue8m0", (P, None, R, 128, 128), -1),
+    ("fgq_quantize_weight_128x128_ue8m0", (None, None, None, 0, 128), 0),
+    ("fgq_gemm_fp8_blockscaled_ue8m0", (P, S1, Q, S2, R, 4, 128, 128, 0, 9), -7),
+    ("fgq_gemm_fp8_blockscaled_ue8m0", (P, S1, Q, S2, R, 4, 128, 128, 5, 0), -4),
+    ("fgq_gemm_fp8_blockscaled_ue8m0", (P, S1, Q, S2, R, 4, 128, 100, 0, 0), -2),
+    ("fgq_gemm_fp8_blockscaled_ue8m0", (P, S1, Q, S2, S1 - 16, 4, 128, 128, 0, 0), -6),
+    ("fgq_gemm_fp8_blockscaled_ue8m0", (None,) * 5 + (0, 128, 128, 0, 0), 0),
+])
+def test_ue8m0_validation(fn, args, want):
+    assert getattr(fgq.load(), fn)(*args, None) == want
