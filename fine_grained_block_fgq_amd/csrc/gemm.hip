@@ -28,6 +28,8 @@
 #include "fgq_device.hpp"
 #include "fgq_launch.hpp"
 
+#include <atomic>
+
 // compile-time tuning knobs (defaults are the shipped configuration)
 #ifndef FGQ_SCHED
 #define FGQ_SCHED 0
@@ -357,7 +359,7 @@ template <class Cfg, class SI, bool OUT_BF16, bool FUSE = false>
 __global__ __launch_bounds__(Cfg::NT) void gemm_fp8_blockscaled_kernel(
     const uint8_t* __restrict__ A, const typename SI::T* __restrict__ sA,
     const uint8_t* __restrict__ B, const typename SI::T* __restrict__ sB,
-    void* __restrict__ Cout, int64_t M, int64_t N, int64_t K,
+    void* __restrict__ Cout, int64_t M, int64_t N, int64_t K, int64_t n_begin, int64_t n_end,
     uint8_t* __restrict__ Cq = nullptr, float* __restrict__ sC = nullptr)
 {
     __shared__ __attribute__((aligned(1024))) uint8_t smem_raw[Cfg::STAGES * Cfg::STAGE];
@@ -369,9 +371,11 @@ __global__ __launch_bounds__(Cfg::NT) void gemm_fp8_blockscaled_kernel(
 
     // tile index: spread consecutive workgroups (which the dispatcher deals round-robin to
     // the 8 XCDs) so that each XCD works on one contiguous range of tiles, then walk that
-    // range in groups of GROUP_M tile rows so neighbours share A and B panels in L2.
+    // range in groups of GROUP_M tile rows so neighbours share A and B panels in L2.  The
+    // launch covers the output columns [n_begin, n_end) (all of them unless the launcher
+    // splits the columns between two tile shapes).
     const int64_t tiles_m = (M + Cfg::BM - 1) / Cfg::BM;
-    const int64_t tiles_n = (N + Cfg::BN - 1) / Cfg::BN;
+    const int64_t tiles_n = (n_end - n_begin + Cfg::BN - 1) / Cfg::BN;
     const int64_t G = (int64_t)gridDim.x;
     int64_t pid = blockIdx.x;
     if (G % 8 == 0)
@@ -382,7 +386,7 @@ __global__ __launch_bounds__(Cfg::NT) void gemm_fp8_blockscaled_kernel(
     const int64_t gsize = (tiles_m - first_m) < GROUP_M ? (tiles_m - first_m) : GROUP_M;
     const int64_t tm = first_m + (pid % gsize);
     const int64_t tn = (pid % (GROUP_M * tiles_n)) / gsize;
-    const int64_t m0 = tm * Cfg::BM, n0 = tn * Cfg::BN;
+    const int64_t m0 = tm * Cfg::BM, n0 = n_begin + tn * Cfg::BN;
 
     const int64_t KB = K / 128, NB = N / 128;
     const int g = lane >> 4;      // k-group of the MFMA operands (32 k each)
@@ -478,22 +482,26 @@ __global__ __launch_bounds__(Cfg::NT) void gemm_fp8_blockscaled_kernel(
     }
 }
 
+// one launch of a wide tile shape over the output columns [n_begin, n_end)
 template <class Cfg, class SI>
 static hipError_t launch_cfg(const void* A_q, const void* sA_, const void* B_q, const void* sB_,
                              void* C, int64_t M, int64_t N, int64_t K, int out_bf16,
-                             hipStream_t stream)
+                             hipStream_t stream, int64_t n_begin = 0, int64_t n_end = -1)
 {
+    if (n_end < 0)
+        n_end = N;
     const typename SI::T* sA = static_cast<const typename SI::T*>(sA_);
     const typename SI::T* sB = static_cast<const typename SI::T*>(sB_);
-    const int64_t tiles = ((M + Cfg::BM - 1) / Cfg::BM) * ((N + Cfg::BN - 1) / Cfg::BN);
+    const int64_t tiles =
+        ((M + Cfg::BM - 1) / Cfg::BM) * ((n_end - n_begin + Cfg::BN - 1) / Cfg::BN);
     if (out_bf16)
         hipLaunchKernelGGL((gemm_fp8_blockscaled_kernel<Cfg, SI, true>), dim3((unsigned)tiles),
                            dim3(Cfg::NT), 0, stream, static_cast<const uint8_t*>(A_q), sA,
-                           static_cast<const uint8_t*>(B_q), sB, C, M, N, K);
+                           static_cast<const uint8_t*>(B_q), sB, C, M, N, K, n_begin, n_end);
     else
         hipLaunchKernelGGL((gemm_fp8_blockscaled_kernel<Cfg, SI, false>), dim3((unsigned)tiles),
                            dim3(Cfg::NT), 0, stream, static_cast<const uint8_t*>(A_q), sA,
-                           static_cast<const uint8_t*>(B_q), sB, C, M, N, K);
+                           static_cast<const uint8_t*>(B_q), sB, C, M, N, K, n_begin, n_end);
     return hipGetLastError();
 }
 
@@ -691,7 +699,7 @@ static hipError_t launch_fused(const void* A_q, const float* sA, const void* B_q
     const int64_t tiles = ((M + Cfg::BM - 1) / Cfg::BM) * ((N + Cfg::BN - 1) / Cfg::BN);
     hipLaunchKernelGGL((gemm_fp8_blockscaled_kernel<Cfg, ScaleIn<false>, true, true>), dim3((unsigned)tiles),
                        dim3(Cfg::NT), 0, stream, static_cast<const uint8_t*>(A_q), sA,
-                       static_cast<const uint8_t*>(B_q), sB, C, M, N, K,
+                       static_cast<const uint8_t*>(B_q), sB, C, M, N, K, (int64_t)0, N,
                        static_cast<uint8_t*>(Cq), sC);
     return hipGetLastError();
 }
@@ -709,11 +717,59 @@ using CfgSmall = GemmCfg<FGQ_SMALL_CFG>;
 #endif
 using CfgNarrow = NarrowCfg<FGQ_NARROW_CFG>;
 
+// compute units of the current device (queried once per device)
+static int device_cus()
+{
+    static std::atomic<int> cache[64];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0)
+        return 0;
+    if (dev < 64) {
+        const int c = cache[dev].load(std::memory_order_relaxed);
+        if (c > 0)
+            return c;
+    }
+    int cus = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+        return 0;
+    if (dev < 64)
+        cache[dev].store(cus, std::memory_order_relaxed);
+    return cus;
+}
+
+// Wave quantization of the 256x128 tiles (one resident workgroup per CU): when the tiles
+// fill R whole rounds of the CUs plus a last round at most half full, and that remainder is
+// whole tile columns, the remainder's columns run as 128x128 tiles instead -- twice as many
+// tiles of half the work, one round of half the duration -- so the last round has no idle
+// half.  Returns the first column of that tail, or N when the split does not apply.
+static int64_t tail_split_column(int64_t M, int64_t N)
+{
+    const int cus = device_cus();
+    const int64_t tm = (M + CfgLarge::BM - 1) / CfgLarge::BM, tn = N / CfgLarge::BN;
+    if (cus <= 0 || tm * tn <= cus)
+        return N;
+    const int64_t r = (tm * tn) % cus;
+    if (r == 0 || 2 * r > cus || r % tm != 0)
+        return N;
+    return N - (r / tm) * CfgLarge::BN;
+}
+
 template <class SI>
 static hipError_t launch_gemm(const void* A_q, const void* sA, const void* B_q, const void* sB,
                               void* C, int64_t M, int64_t N, int64_t K, int out_bf16,
                               int variant, hipStream_t stream)
 {
+    if (variant == GEMM_AUTO && M >= 256) {
+        const int64_t split = tail_split_column(M, N);
+        if (split < N) {
+            const hipError_t e = launch_cfg<CfgLarge, SI>(A_q, sA, B_q, sB, C, M, N, K, out_bf16,
+                                                          stream, 0, split);
+            if (e != hipSuccess)
+                return e;
+            return launch_cfg<CfgSmall, SI>(A_q, sA, B_q, sB, C, M, N, K, out_bf16, stream,
+                                            split, N);
+        }
+    }
     if (variant == GEMM_AUTO) {
         // wide tiles while they fill the 256 CUs at least once, else narrow tiles
         const int64_t tiles_large = ((M + CfgLarge::BM - 1) / CfgLarge::BM) * (N / CfgLarge::BN);

@@ -107,3 +107,16 @@ def test_large_workload_sampled(name):
     assert np.array_equal(Cf, Cf2)
     del Cb, Cf, Cf2
     free()
+
+
+@pytest.mark.parametrize("out", ["f32", "bf16"])
+def test_wave_tail_split(out):
+    """256 x 38400: 300 tiles of 256x128 on 256 CUs leave a last round of 44; those columns
+    run as 128x128 tiles in a second launch.  Every element against the oracle."""
+    M, N, K = 256, 38400, 256
+    log(f"gemm tail split M={M} N={N} K={K} {out}")
+    Aq, sA, Bq, sB = random_operands(M, N, K, seed=99)
+    C = gpu_gemm(Aq, sA, Bq, sB, torch.float32 if out == "f32" else torch.bfloat16)
+    Cr, S = oracle.gemm_f64(Aq, sA, Bq, sB)
+    assert gemm_error_ratio(C, Cr, S, out == "bf16") <= 1.0
+    free()
