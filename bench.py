@@ -81,10 +81,16 @@ def summarize(ktrace_dir, fetch_dir, write_dir):
             return list(csv.DictReader(fh))
 
     def short(name):
-        for k in ("gemm_fp8_blockscaled_kernel", "quant_act_1x128_kernel",
-                  "quant_weight_128x128_kernel", "vectorized_elementwise_kernel"):
+        for k in ("gemm_fp8_blockscaled_narrow_kernel", "gemm_fp8_blockscaled_kernel",
+                  "quant_act_1x128_kernel", "quant_weight_128x128_kernel",
+                  "vectorized_elementwise_kernel"):
             if k in name:
-                return k
+                tags = ""
+                if "ScaleIn<true>" in name or "ScaleUE8M0" in name:
+                    tags += "+ue8m0"
+                if k == "gemm_fp8_blockscaled_kernel" and ", true, true>" in name:
+                    tags += "+fused"
+                return k + tags
         return name[:60]
 
     os.makedirs(PROFILES, exist_ok=True)
@@ -94,9 +100,9 @@ def summarize(ktrace_dir, fetch_dir, write_dir):
     for r in trace:
         key = (short(r["Kernel_Name"]), int(r["Grid_Size_X"] if "Grid_Size_X" in r else r.get("Grid_Size", 0)))
         groups.setdefault(key, []).append(int(r["End_Timestamp"]) - int(r["Start_Timestamp"]))
-    lines = [f"{'kernel':34s} {'grid':>9s} {'calls':>6s} {'avg_us':>9s} {'min_us':>9s} {'max_us':>9s}"]
+    lines = [f"{'kernel':40s} {'grid':>9s} {'calls':>6s} {'avg_us':>9s} {'min_us':>9s} {'max_us':>9s}"]
     for (name, grid), d in sorted(groups.items()):
-        lines.append(f"{name:34s} {grid:9d} {len(d):6d} {sum(d)/len(d)/1e3:9.2f} {min(d)/1e3:9.2f} {max(d)/1e3:9.2f}")
+        lines.append(f"{name:40s} {grid:9d} {len(d):6d} {sum(d)/len(d)/1e3:9.2f} {min(d)/1e3:9.2f} {max(d)/1e3:9.2f}")
     stats = "\n".join(lines)
     # counters
     def counter(d, cname):
@@ -123,12 +129,12 @@ def summarize(ktrace_dir, fetch_dir, write_dir):
     out = ["rocprofv3 byte counters per dispatch (KiB), scaled by the 512 MiB copy calibration",
            f"calibration: copy FETCH_SIZE {fetch[fk]:.1f} KiB -> x{fetch_scale:.3f}; "
            f"WRITE_SIZE {write[fk]:.1f} KiB -> x{write_scale:.3f}",
-           f"{'kernel':34s} {'grid':>9s} {'FETCH_KiB':>12s} {'WRITE_KiB':>12s} {'HBM_MB(scaled)':>15s}"]
+           f"{'kernel':40s} {'grid':>9s} {'FETCH_KiB':>12s} {'WRITE_KiB':>12s} {'HBM_MB(scaled)':>15s}"]
     for k in sorted(fetch):
         if k not in write:
             continue
         b = fetch[k] * 1024 * fetch_scale + write[k] * 1024 * write_scale
-        out.append(f"{k[0]:34s} {k[1]:9d} {fetch[k]:12.1f} {write[k]:12.1f} {b/1e6:15.2f}")
+        out.append(f"{k[0]:40s} {k[1]:9d} {fetch[k]:12.1f} {write[k]:12.1f} {b/1e6:15.2f}")
         if k == ("gemm_fp8_blockscaled_kernel", 262144):
             traffic["gemm_fp8_blockscaled 4096^3 bf16"] = {"source_sha256": source_hash("gemm"),
                                                           "bytes_per_launch": b}
@@ -324,6 +330,29 @@ def main():
     log(f"fused GEMM+quant {fused_ms*1e3:.1f} us vs GEMM then quantize {sep_ms*1e3:.1f} us")
     del Cq, sC
 
+    # ---- the same step on UE8M0 (power-of-two exponent byte) scales ----------------------
+    eA = torch.empty((M, K // 128), dtype=torch.uint8, device=dev)
+    eB = torch.empty((K // 128, N // 128), dtype=torch.uint8, device=dev)
+    uev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(reps)]
+    for r in range(reps + 3):
+        e = uev[r - 3] if r >= 3 else None
+        if e is not None:
+            e[0].record(stream)
+        fgq.fgq_quantize_act_1x128_ue8m0(A, Aq, eA, stream)
+        if e is not None:
+            e[1].record(stream)
+        fgq.fgq_quantize_weight_128x128_ue8m0(B, Bq, eB, stream)
+        if e is not None:
+            e[2].record(stream)
+        fgq.fgq_gemm_fp8_blockscaled_ue8m0(Aq, eA, Bq, eB, C, stream=stream)
+        if e is not None:
+            e[3].record(stream)
+    torch.cuda.synchronize()
+    ue_ms = [float(np.mean([e[i].elapsed_time(e[i + 1]) for e in uev])) for i in range(3)]
+    log(f"ue8m0: quant A {ue_ms[0]*1e3:.1f} us  quant B {ue_ms[1]*1e3:.1f} us  "
+        f"GEMM {ue_ms[2]*1e3:.1f} us")
+    del eA, eB
+
     # ---- standalone activation quantizer, X [16384,7168] (rotating buffers) -------------
     wq = synth.WORKLOADS["actq"]
     Mq, Kq = wq.M, wq.K
@@ -399,6 +428,13 @@ def main():
             "fused_us": round(fused_ms * 1e3, 2),
             "separate_us": round(sep_ms * 1e3, 2),
             "saved_us": round((sep_ms - fused_ms) * 1e3, 2),
+        },
+        "ue8m0": {
+            "workload": "the 4096^3 step on UE8M0 exponent-byte scales",
+            "quantize_act_us": round(ue_ms[0] * 1e3, 2),
+            "quantize_weight_us": round(ue_ms[1] * 1e3, 2),
+            "gemm_us": round(ue_ms[2] * 1e3, 2),
+            "gemm_tflops": round(flops / (ue_ms[2] * 1e-3) / 1e12, 1),
         },
         "cpu_baseline": None,
     }
