@@ -63,6 +63,15 @@ def _load():
     lib.oracle_quantize_act_1x128_ue8m0.argtypes = [p, p, p, i64, i64, i64, i64]
     lib.oracle_quantize_weight_128x128_ue8m0.restype = ctypes.c_int
     lib.oracle_quantize_weight_128x128_ue8m0.argtypes = [p, p, p, i64, i64, i64, i64]
+    lib.oracle_e2m1_decode.restype = ctypes.c_double
+    lib.oracle_e2m1_decode.argtypes = [ctypes.c_uint8]
+    lib.oracle_e2m1_encode.restype = ctypes.c_uint8
+    lib.oracle_e2m1_encode.argtypes = [ctypes.c_float]
+    lib.oracle_quantize_nvfp4.restype = ctypes.c_int
+    lib.oracle_quantize_nvfp4.argtypes = [p, p, p, p, i64, i64]
+    lib.oracle_gemm_nvfp4_f64.restype = ctypes.c_int
+    lib.oracle_gemm_nvfp4_f64.argtypes = [p, p, ctypes.c_float, p, p, ctypes.c_float, i64, i64,
+                                          i64, p, p, i64, i64]
     lib.oracle_gemm_f64.restype = ctypes.c_int
     lib.oracle_gemm_f64.argtypes = [p, p, p, p, i64, i64, i64, p, p, i64, i64]
     lib.oracle_gemm_f64_at.restype = ctypes.c_int
@@ -185,6 +194,56 @@ def quantize_weight_ue8m0(W_bits: np.ndarray, nthreads: int | None = None):
                                                               a, b),
          _split(K // 128, nt * 2), nt)
     return Wq, sW
+
+
+def e2m1_decode(codes) -> np.ndarray:
+    """Value of each E2M1 code (low 4 bits), by the oracle."""
+    lib = _load()
+    table = np.array([lib.oracle_e2m1_decode(c) for c in range(16)], dtype=np.float64)
+    return table[np.asarray(codes, dtype=np.uint8) & 15]
+
+
+def e2m1_encode(y) -> np.ndarray:
+    """Nearest E2M1 code (ties to even, saturating at 6) of each fp32 value."""
+    lib = _load()
+    y = np.asarray(y, dtype=np.float32)
+    return np.array([lib.oracle_e2m1_encode(float(v)) for v in y.reshape(-1)],
+                    dtype=np.uint8).reshape(y.shape)
+
+
+def quantize_nvfp4(X_bits: np.ndarray):
+    """NVFP4 of bf16 bits X [R, C] -> (packed codes [R, C/2], E4M3 block scales [R, C/16],
+    fp32 global scale)."""
+    lib = _load()
+    X = np.ascontiguousarray(X_bits, dtype=np.uint16)
+    R, C = X.shape
+    if C % 16:
+        raise ValueError("C must be a multiple of 16")
+    Xq = np.empty((R, C // 2), dtype=np.uint8)
+    sX = np.empty((R, C // 16), dtype=np.uint8)
+    g = np.zeros(1, dtype=np.float32)
+    if lib.oracle_quantize_nvfp4(_ptr(X), _ptr(Xq), _ptr(sX), _ptr(g), R, C) != 0:
+        raise ValueError("bad shape")
+    return Xq, sX, np.float32(g[0])
+
+
+def gemm_nvfp4_f64(Aq, sA, gA, Bq, sB, gB, nthreads: int | None = None):
+    """fp64 NVFP4 GEMM reference: (C [M,N], S [M,N]) for A [M,K] and B stored [N,K]."""
+    lib = _load()
+    Aq = np.ascontiguousarray(Aq, dtype=np.uint8)
+    Bq = np.ascontiguousarray(Bq, dtype=np.uint8)
+    sA = np.ascontiguousarray(sA, dtype=np.uint8)
+    sB = np.ascontiguousarray(sB, dtype=np.uint8)
+    M, N, K = Aq.shape[0], Bq.shape[0], Aq.shape[1] * 2
+    if Bq.shape[1] * 2 != K or sA.shape != (M, K // 16) or sB.shape != (N, K // 16):
+        raise ValueError("shape mismatch")
+    C = np.empty((M, N), dtype=np.float64)
+    S = np.empty((M, N), dtype=np.float64)
+    nt = nthreads or threads()
+    _run(lambda a, b: lib.oracle_gemm_nvfp4_f64(_ptr(Aq), _ptr(sA), float(gA), _ptr(Bq), _ptr(sB),
+                                                float(gB), M, N, K, _ptr(C), _ptr(S), a, b),
+         _split(M, nt * 4), nt)
+    return C, S
 
 
 def _gemm_args(Aq, sA, Bq, sB):

@@ -27,6 +27,7 @@
  * binary64 operation with round-to-nearest-even, as written).
  */
 #include <math.h>
+#include <stdlib.h>
 #include <stdint.h>
 #include <string.h>
 
@@ -323,6 +324,141 @@ int oracle_quantize_weight_128x128_ue8m0(const uint16_t *W, uint8_t *Wq, uint8_t
                     idx[t++] = (kb * 128 + r) * N + nb * 128 + c;
             sW[kb * NB + nb] = quantize_group_ue8m0(W, idx, 128 * 128, Wq);
         }
+    return 0;
+}
+
+/* ------------------------------------------------------------------------------------ */
+/* NVFP4 two-level scaling (page "Fine-Grained FP8/FP4 Quantization", section "NVFP4     */
+/* Two-Level Scaling"): E2M1 codes (magnitudes 0, 0.5, 1, 1.5, 2, 3, 4, 6), one E4M3     */
+/* block scale per 16 consecutive elements along K ([M, K/16] for A), one FP32 global    */
+/* scale per tensor, dequantized as global * block * e2m1.  The page gives the format and */
+/* the dequantization only; the readings used here to pick the scales:                   */
+/*   g  = fl32(amax_tensor / 2688)          (2688 = 448 * 6: the largest block scale is  */
+/*                                           448 and the largest code 6)                 */
+/*   sb = ENC_E4M3(fl32(amax_block / fl32(6 * g)))   (saturating, nearest-even)          */
+/*   D  = fl32(DEC_E4M3(sb) * g)            the block's dequantization multiplier        */
+/*   code = ENC_E2M1(fl32(x / D))           nearest, ties to the even code, saturating   */
+/*                                           at 6; signed zero when D == 0               */
+/* Both operands of the GEMM are row-major [rows, K] with the blocks along K (the weight */
+/* is stored as its [N, K] transpose), two codes per byte, element 2i in the low nibble. */
+/* ------------------------------------------------------------------------------------ */
+
+static const double E2M1_MAG[8] = {0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0};
+
+/* Value of one E2M1 code (low 4 bits: sign bit 3, magnitude code 0..7). */
+double oracle_e2m1_decode(uint8_t code)
+{
+    double v = E2M1_MAG[code & 7];
+    return (code & 8) ? -v : v;
+}
+
+/* Nearest E2M1 code of y; a tie goes to the even magnitude code; |y| >= 6 gives 6. */
+uint8_t oracle_e2m1_encode(float y)
+{
+    uint8_t sign = signbit(y) ? 8 : 0;
+    double a = fabs((double)y);
+    uint8_t best = 7;
+    if (a < 6.0) {
+        for (uint8_t c = 0; c < 7; ++c) {
+            double lo = E2M1_MAG[c], hi = E2M1_MAG[c + 1];
+            if (a <= hi) {
+                double mid = 0.5 * (lo + hi);   /* exact in binary64 */
+                if (a < mid)
+                    best = c;
+                else if (a > mid)
+                    best = c + 1;
+                else
+                    best = (c % 2 == 0) ? c : c + 1;
+                break;
+            }
+        }
+    }
+    return sign | best;
+}
+
+/*
+ * NVFP4 quantization of a row-major bf16 matrix X [R, C] (C % 16 == 0), blocks of 16 along
+ * C.  Xq: [R, C/2] packed codes; sX: [R, C/16] E4M3 block scales; *g: the global scale.
+ * Single-threaded (the tensor amax couples every element).
+ */
+int oracle_quantize_nvfp4(const uint16_t *X, uint8_t *Xq, uint8_t *sX, float *g, int64_t R,
+                          int64_t C)
+{
+    if (R < 0 || C < 0 || C % 16 != 0)
+        return -1;
+    float amax_t = 0.0f;
+    for (int64_t i = 0; i < R * C; ++i) {
+        float v = fabsf(bf16_to_f32(X[i]));
+        if (v > amax_t)
+            amax_t = v;
+    }
+    float gs = amax_t / 2688.0f;
+    *g = gs;
+    float six_g = 6.0f * gs;
+    int64_t CB = C / 16;
+    for (int64_t r = 0; r < R; ++r) {
+        for (int64_t b = 0; b < CB; ++b) {
+            const uint16_t *xb = X + r * C + b * 16;
+            float amax_b = 0.0f;
+            for (int j = 0; j < 16; ++j) {
+                float v = fabsf(bf16_to_f32(xb[j]));
+                if (v > amax_b)
+                    amax_b = v;
+            }
+            uint8_t sb = (six_g == 0.0f) ? 0 : oracle_e4m3_encode(amax_b / six_g);
+            sX[r * CB + b] = sb;
+            float D = (float)oracle_e4m3_decode(sb) * gs;
+            for (int j = 0; j < 16; j += 2) {
+                uint8_t c[2];
+                for (int h = 0; h < 2; ++h) {
+                    float x = bf16_to_f32(xb[j + h]);
+                    c[h] = (D == 0.0f) ? (signbit(x) ? 8 : 0) : oracle_e2m1_encode(x / D);
+                }
+                Xq[(r * C + b * 16 + j) / 2] = (uint8_t)(c[0] | (c[1] << 4));
+            }
+        }
+    }
+    return 0;
+}
+
+/*
+ * NVFP4 GEMM reference, rows m0 <= m < m1:  C[m,n] = sum_k a[m,k] b[n,k] with
+ * a = gA * dec(sA[m,k/16]) * e2m1(A_q[m,k]) and b = gB * dec(sB[n,k/16]) * e2m1(B_q[n,k])
+ * in fp64 (k ascending); S = sum |a b|.  A_q [M, K/2], B_q [N, K/2] packed; K % 16 == 0.
+ */
+int oracle_gemm_nvfp4_f64(const uint8_t *Aq, const uint8_t *sA, float gA, const uint8_t *Bq,
+                          const uint8_t *sB, float gB, int64_t M, int64_t N, int64_t K,
+                          double *C, double *S, int64_t m0, int64_t m1)
+{
+    if (M < 0 || N < 0 || K < 0 || K % 16 != 0 || m0 < 0 || m1 > M || m0 > m1)
+        return -1;
+    int64_t KB = K / 16;
+    double *arow = (double *)malloc(sizeof(double) * (size_t)(K > 0 ? K : 1));
+    if (!arow)
+        return -1;
+    for (int64_t m = m0; m < m1; ++m) {
+        for (int64_t k = 0; k < K; ++k) {
+            uint8_t byte = Aq[(m * K + k) / 2];
+            uint8_t code = (k % 2 == 0) ? (byte & 15) : (byte >> 4);
+            arow[k] = (double)gA * oracle_e4m3_decode(sA[m * KB + k / 16]) * oracle_e2m1_decode(code);
+        }
+        for (int64_t n = 0; n < N; ++n) {
+            double c = 0.0, s = 0.0;
+            for (int64_t k = 0; k < K; ++k) {
+                uint8_t byte = Bq[(n * K + k) / 2];
+                uint8_t code = (k % 2 == 0) ? (byte & 15) : (byte >> 4);
+                double b = (double)gB * oracle_e4m3_decode(sB[n * KB + k / 16]) *
+                           oracle_e2m1_decode(code);
+                double p = arow[k] * b;
+                c += p;
+                s += fabs(p);
+            }
+            C[m * N + n] = c;
+            if (S)
+                S[m * N + n] = s;
+        }
+    }
+    free(arow);
     return 0;
 }
 
