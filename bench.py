@@ -82,6 +82,7 @@ def summarize(ktrace_dir, fetch_dir, write_dir):
 
     def short(name):
         for k in ("gemm_fp8_blockscaled_narrow_kernel", "gemm_fp8_blockscaled_kernel",
+                  "gemm_nvfp4_kernel", "nvfp4_quant_kernel", "nvfp4_amax_kernel",
                   "quant_act_1x128_kernel", "quant_weight_128x128_kernel",
                   "vectorized_elementwise_kernel"):
             if k in name:
@@ -353,6 +354,35 @@ def main():
         f"GEMM {ue_ms[2]*1e3:.1f} us")
     del eA, eB
 
+    # ---- NVFP4: the same shapes with E2M1 codes, per-16 E4M3 and global fp32 scales; the
+    # weight is quantized from its [N, K] transpose ----------------------------------------
+    Bt = B.t().contiguous()
+    A4 = torch.empty((M, K // 2), dtype=torch.uint8, device=dev)
+    sA4 = torch.empty((M, K // 16), dtype=torch.uint8, device=dev)
+    gA4 = torch.empty((1,), dtype=torch.float32, device=dev)
+    B4 = torch.empty((N, K // 2), dtype=torch.uint8, device=dev)
+    sB4 = torch.empty((N, K // 16), dtype=torch.uint8, device=dev)
+    gB4 = torch.empty((1,), dtype=torch.float32, device=dev)
+    nev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(reps)]
+    for r in range(reps + 3):
+        e = nev[r - 3] if r >= 3 else None
+        if e is not None:
+            e[0].record(stream)
+        fgq.fgq_quantize_nvfp4(A, A4, sA4, gA4, stream)
+        if e is not None:
+            e[1].record(stream)
+        fgq.fgq_quantize_nvfp4(Bt, B4, sB4, gB4, stream)
+        if e is not None:
+            e[2].record(stream)
+        fgq.fgq_gemm_nvfp4(A4, sA4, gA4, B4, sB4, gB4, C, stream=stream)
+        if e is not None:
+            e[3].record(stream)
+    torch.cuda.synchronize()
+    nv_ms = [float(np.mean([e[i].elapsed_time(e[i + 1]) for e in nev])) for i in range(3)]
+    log(f"nvfp4: quant A {nv_ms[0]*1e3:.1f} us  quant B {nv_ms[1]*1e3:.1f} us  "
+        f"GEMM {nv_ms[2]*1e3:.1f} us")
+    del Bt, A4, sA4, gA4, B4, sB4, gB4
+
     # ---- standalone activation quantizer, X [16384,7168] (rotating buffers) -------------
     wq = synth.WORKLOADS["actq"]
     Mq, Kq = wq.M, wq.K
@@ -435,6 +465,13 @@ def main():
             "quantize_weight_us": round(ue_ms[1] * 1e3, 2),
             "gemm_us": round(ue_ms[2] * 1e3, 2),
             "gemm_tflops": round(flops / (ue_ms[2] * 1e-3) / 1e12, 1),
+        },
+        "nvfp4": {
+            "workload": "the 4096^3 step in NVFP4 (E2M1, per-16 E4M3 + fp32 global scales)",
+            "quantize_act_us": round(nv_ms[0] * 1e3, 2),
+            "quantize_weight_us": round(nv_ms[1] * 1e3, 2),
+            "gemm_us": round(nv_ms[2] * 1e3, 2),
+            "gemm_tflops": round(flops / (nv_ms[2] * 1e-3) / 1e12, 1),
         },
         "cpu_baseline": None,
     }

@@ -18,7 +18,7 @@ __all__ = [
     "fgq_quantize_weight_128x128", "fgq_gemm_fp8_blockscaled",
     "fgq_gemm_fp8_blockscaled_variant", "fgq_gemm_fp8_blockscaled_quant",
     "fgq_quantize_act_1x128_ue8m0", "fgq_quantize_weight_128x128_ue8m0",
-    "fgq_gemm_fp8_blockscaled_ue8m0", "FGQ_OUT_F32", "FGQ_OUT_BF16", "FGQ_GEMM_AUTO",
+    "fgq_gemm_fp8_blockscaled_ue8m0", "fgq_quantize_nvfp4", "fgq_gemm_nvfp4", "FGQ_OUT_F32", "FGQ_OUT_BF16", "FGQ_GEMM_AUTO",
     "FGQ_GEMM_WIDE_256x128", "FGQ_GEMM_WIDE_128x128", "FGQ_GEMM_NARROW_64x32",
 ]
 
@@ -62,6 +62,10 @@ def load() -> ctypes.CDLL:
     lib.fgq_quantize_weight_128x128_ue8m0.argtypes = [p, p, p, i64, i64, p]
     lib.fgq_gemm_fp8_blockscaled_ue8m0.restype = i32
     lib.fgq_gemm_fp8_blockscaled_ue8m0.argtypes = [p, p, p, p, p, i64, i64, i64, i32, i32, p]
+    lib.fgq_quantize_nvfp4.restype = i32
+    lib.fgq_quantize_nvfp4.argtypes = [p, p, p, p, i64, i64, p]
+    lib.fgq_gemm_nvfp4.restype = i32
+    lib.fgq_gemm_nvfp4.argtypes = [p, p, p, p, p, p, p, i64, i64, i64, i32, p]
     lib.fgq_gemm_fp8_blockscaled_quant.restype = i32
     lib.fgq_gemm_fp8_blockscaled_quant.argtypes = [p, p, p, p, p, p, p, i64, i64, i64, p]
     lib.fgq_status_string.restype = ctypes.c_char_p
@@ -248,4 +252,52 @@ def fgq_gemm_fp8_blockscaled_ue8m0(A_q: torch.Tensor, scale_A: torch.Tensor,
         _dev(B_q, "B_q", _codes_dtype(B_q), (K, N)),
         _dev(scale_B, "scale_B", torch.uint8, (K // 128, N // 128)),
         _dev(C, "C", C.dtype, (M, N)), M, N, K, code, int(variant), _stream(stream)))
+    return C
+
+
+def fgq_quantize_nvfp4(X: torch.Tensor, Xq: torch.Tensor | None = None,
+                       scale_X: torch.Tensor | None = None,
+                       global_scale: torch.Tensor | None = None, stream=None):
+    """NVFP4 of bf16 X [R, C] (blocks of 16 along C): (packed codes uint8 [R, C/2], E4M3
+    block scales uint8 [R, C/16], fp32 global scale [1])."""
+    lib = load()
+    R, C = X.shape
+    dev = X.device
+    if Xq is None:
+        Xq = torch.empty((R, C // 2), dtype=torch.uint8, device=dev)
+    if scale_X is None:
+        scale_X = torch.empty((R, C // 16), dtype=torch.uint8, device=dev)
+    if global_scale is None:
+        global_scale = torch.empty((1,), dtype=torch.float32, device=dev)
+    _check("fgq_quantize_nvfp4", lib.fgq_quantize_nvfp4(
+        _dev(X, "X", torch.bfloat16, (R, C)), _dev(Xq, "Xq", torch.uint8, (R, C // 2)),
+        _dev(scale_X, "scale_X", torch.uint8, (R, C // 16)),
+        _dev(global_scale, "global_scale", torch.float32, (1,)), R, C, _stream(stream)))
+    return Xq, scale_X, global_scale
+
+
+def fgq_gemm_nvfp4(A_q: torch.Tensor, scale_A: torch.Tensor, global_A: torch.Tensor,
+                   B_q: torch.Tensor, scale_B: torch.Tensor, global_B: torch.Tensor,
+                   C: torch.Tensor | None = None, out_dtype: torch.dtype = torch.bfloat16,
+                   stream=None):
+    """NVFP4 GEMM: A [M, K] and the weight stored as its transpose [N, K] (both packed)."""
+    lib = load()
+    M, K2 = A_q.shape
+    N, K2b = B_q.shape
+    if K2 != K2b:
+        raise ValueError(f"A_q is [{M},{K2}] bytes but B_q is [{N},{K2b}]")
+    K = 2 * K2
+    if C is None:
+        C = torch.empty((M, N), dtype=out_dtype, device=A_q.device)
+    code = {torch.float32: FGQ_OUT_F32, torch.bfloat16: FGQ_OUT_BF16}.get(C.dtype)
+    if code is None:
+        raise TypeError(f"C must be float32 or bfloat16, got {C.dtype}")
+    _check("fgq_gemm_nvfp4", lib.fgq_gemm_nvfp4(
+        _dev(A_q, "A_q", torch.uint8, (M, K // 2)),
+        _dev(scale_A, "scale_A", torch.uint8, (M, K // 16)),
+        _dev(global_A, "global_A", torch.float32, (1,)),
+        _dev(B_q, "B_q", torch.uint8, (N, K // 2)),
+        _dev(scale_B, "scale_B", torch.uint8, (N, K // 16)),
+        _dev(global_B, "global_B", torch.float32, (1,)),
+        _dev(C, "C", C.dtype, (M, N)), M, N, K, code, _stream(stream)))
     return C

@@ -215,4 +215,57 @@ int fgq_gemm_fp8_blockscaled_quant(const void* A_q, const float* scale_A, const 
         A_q, scale_A, B_q, scale_B, C, C_q, scale_C, M, N, K, static_cast<hipStream_t>(stream)));
 }
 
+int fgq_quantize_nvfp4(const void* X, void* Xq, uint8_t* scale_X, float* global_scale,
+                       int64_t R, int64_t C, void* stream)
+{
+    if (R < 0 || C < 0 || C % 16 != 0 || R > kMaxDim || C > kMaxDim)
+        return FGQ_ERR_SHAPE;
+    if (R > 0 && C > 0 && R > ((int64_t(1) << 38) / C))
+        return FGQ_ERR_SHAPE;
+    if (R == 0 || C == 0)
+        return FGQ_OK;
+    if (!X || !Xq || !scale_X || !global_scale)
+        return FGQ_ERR_NULL;
+    if (misaligned(X) || misaligned(Xq) || misaligned(scale_X) || misaligned(global_scale))
+        return FGQ_ERR_ALIGN;
+    const void* p[4] = {X, Xq, scale_X, global_scale};
+    const int64_t n[4] = {2 * R * C, R * C / 2, R * (C / 16), 4};
+    for (int a = 0; a < 4; ++a)
+        for (int b = a + 1; b < 4; ++b)
+            if (overlap(p[a], n[a], p[b], n[b]))
+                return FGQ_ERR_ALIAS;
+    return launch_status(fgq::launch_quant_nvfp4(X, Xq, scale_X, global_scale, R, C,
+                                                 static_cast<hipStream_t>(stream)));
+}
+
+int fgq_gemm_nvfp4(const void* A_q, const uint8_t* scale_A, const float* global_A,
+                   const void* B_q, const uint8_t* scale_B, const float* global_B, void* C,
+                   int64_t M, int64_t N, int64_t K, int out_dtype, void* stream)
+{
+    if (out_dtype != FGQ_OUT_F32 && out_dtype != FGQ_OUT_BF16)
+        return FGQ_ERR_DTYPE;
+    if (M < 0 || N < 0 || K < 0 || K % 128 != 0 || N % 128 != 0 || M > kMaxDim ||
+        N > kMaxDim || K > kMaxDim)
+        return FGQ_ERR_SHAPE;
+    if (((M + 127) / 128) * (N / 128) > kMaxDim)
+        return FGQ_ERR_SHAPE;
+    if (M == 0 || N == 0)
+        return FGQ_OK;
+    if (!C || !global_A || !global_B || (K > 0 && (!A_q || !scale_A || !B_q || !scale_B)))
+        return FGQ_ERR_NULL;
+    if (misaligned(C) || misaligned(global_A) || misaligned(global_B) ||
+        (K > 0 && (misaligned(A_q) || misaligned(scale_A) || misaligned(B_q) ||
+                   misaligned(scale_B))))
+        return FGQ_ERR_ALIGN;
+    const int64_t nc = M * N * (out_dtype == FGQ_OUT_BF16 ? 2 : 4);
+    if (overlap(C, nc, global_A, 4) || overlap(C, nc, global_B, 4) ||
+        (K > 0 && (overlap(C, nc, A_q, M * K / 2) || overlap(C, nc, B_q, N * K / 2) ||
+                   overlap(C, nc, scale_A, M * (K / 16)) ||
+                   overlap(C, nc, scale_B, N * (K / 16)))))
+        return FGQ_ERR_ALIAS;
+    return launch_status(fgq::launch_gemm_nvfp4(A_q, scale_A, global_A, B_q, scale_B, global_B,
+                                                C, M, N, K, out_dtype == FGQ_OUT_BF16,
+                                                static_cast<hipStream_t>(stream)));
+}
+
 }  // extern "C"

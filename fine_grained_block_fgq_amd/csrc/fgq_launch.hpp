@@ -35,4 +35,12 @@ hipError_t launch_gemm_fp8_blockscaled_quant(const void* A_q, const float* sA, c
                                              int64_t M, int64_t N, int64_t K,
                                              hipStream_t stream);
 
+// NVFP4: quantize X [R,C] (blocks of 16 along C) to packed E2M1 codes [R,C/2], E4M3 block
+// scales [R,C/16] and the fp32 global scale *g; GEMM of A [M,K] and B stored [N,K]
+hipError_t launch_quant_nvfp4(const void* X, void* Xq, uint8_t* sX, float* g, int64_t R,
+                              int64_t C, hipStream_t stream);
+hipError_t launch_gemm_nvfp4(const void* A_q, const uint8_t* sA, const float* gA,
+                             const void* B_q, const uint8_t* sB, const float* gB, void* C,
+                             int64_t M, int64_t N, int64_t K, int out_bf16, hipStream_t stream);
+
 }  // namespace fgq

@@ -27,6 +27,7 @@
 //     per chunk (a wave's columns never straddle a 128-column block).
 #include "fgq_device.hpp"
 #include "fgq_launch.hpp"
+#include "gemm_common.hpp"
 
 #include <atomic>
 
@@ -42,24 +43,6 @@
 #endif
 
 namespace fgq {
-
-typedef int i32x8 __attribute__((ext_vector_type(8)));
-typedef int i32x4 __attribute__((ext_vector_type(4)));
-typedef int i32x2 __attribute__((ext_vector_type(2)));
-typedef float f32x4 __attribute__((ext_vector_type(4)));
-typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
-typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
-
-// 8 E4M3 codes (two dwords) -> 8 f16, exact
-__device__ __forceinline__ f16x8 e4m3x8_to_f16(int w0, int w1)
-{
-    const f16x2 a = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w0, 1.0f, false);
-    const f16x2 b = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w0, 1.0f, true);
-    const f16x2 c = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w1, 1.0f, false);
-    const f16x2 d = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w1, 1.0f, true);
-    return f16x8{a[0], a[1], b[0], b[1], c[0], c[1], d[0], d[1]};
-}
-#define LDS __attribute__((address_space(3)))
 
 template <int BM_, int BN_, int WM_, int WN_, int STAGES_>
 struct GemmCfg {
@@ -109,54 +92,6 @@ struct GemmCfg {
     static constexpr int MIN_LOADS = (A_LOADS + B_LOADS) / NW;
 };
 
-// s_waitcnt vmcnt(N) (gfx9 encoding: vmcnt bits [3:0] and [15:14]; expcnt [6:4] and
-// lgkmcnt [11:8] left at their maxima, i.e. not waited on)
-template <int N>
-__device__ __forceinline__ void wait_vm()
-{
-    static_assert(N >= 0 && N < 64, "vmcnt range");
-    __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
-}
-
-// workgroup barrier that orders LDS accesses only (no wait on outstanding global loads)
-__device__ __forceinline__ void lds_barrier()
-{
-    // lgkmcnt(0): this wave's LDS reads have returned (vmcnt/expcnt not waited on)
-    __builtin_amdgcn_s_waitcnt(0xC07F);
-    asm volatile("" ::: "memory");
-    __builtin_amdgcn_s_barrier();
-    asm volatile("" ::: "memory");
-}
-
-// One direct-to-LDS load: 16 bytes per lane from gptr to LDS [lds + 16*lane] (or 4 bytes
-// per lane to [lds + 4*lane]).  Written as inline asm so the compiler's wait-count pass
-// does not see an outstanding LDS write and does not put a vmcnt(0) in front of every LDS
-// read of the other stage; the pipeline waits for these loads explicitly (wait_vm).
-// M0 holds the LDS base; one wait state separates the M0 write from its use.
-__device__ __forceinline__ void dma_b128(const void* gptr, uint32_t lds)
-{
-    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
-                 :
-                 : "v"(gptr), "s"(lds)
-                 : "memory", "m0");
-}
-__device__ __forceinline__ void dma_b32(const void* gptr, uint32_t lds)
-{
-    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dword %0, off"
-                 :
-                 : "v"(gptr), "s"(lds)
-                 : "memory", "m0");
-}
-
-// one byte per lane, zero-extended into the lane's dword slot [lds + 4*lane]
-__device__ __forceinline__ void dma_u8(const void* gptr, uint32_t lds)
-{
-    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_ubyte %0, off"
-                 :
-                 : "v"(gptr), "s"(lds)
-                 : "memory", "m0");
-}
-
 // Scale formats the GEMM reads: fp32 scales, or UE8M0 exponent bytes e standing for
 // 2^(e-127) (page "Fine-Grained FP8/FP4 Quantization", section "Blackwell: Native Block
 // Scaling").  Either way one 4-byte LDS slot per tile row carries scale_A of the chunk, and
@@ -190,10 +125,6 @@ struct ScaleIn<true> {
     }
 };
 
-__device__ __forceinline__ uint32_t lds_addr(const uint8_t LDS* p)
-{
-    return (uint32_t)(uintptr_t)p;
-}
 
 template <class Cfg, class SI>
 __device__ __forceinline__ void load_stage(uint8_t LDS* stage, const uint8_t* __restrict__ A,

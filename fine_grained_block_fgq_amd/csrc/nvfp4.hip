@@ -1,0 +1,342 @@
+// nvfp4.hip -- NVFP4 (two-level scaled E2M1) quantization and GEMM for gfx950.
+//
+// Page "Fine-Grained FP8/FP4 Quantization", section "NVFP4 Two-Level Scaling": E2M1 codes
+// (magnitudes 0, 0.5, 1, 1.5, 2, 3, 4, 6), one E4M3 block scale per 16 consecutive elements
+// along K, one FP32 global scale per tensor; value = global * block * e2m1.  Scales are
+// chosen as g = amax/2688 (the largest block scale 448 times the largest code 6), block =
+// E4M3(amax_block / (6g)), code = E2M1(x / (block * g)) nearest-even, saturating at 6.
+// Both GEMM operands are row-major [rows, K] with K contiguous (the weight is stored as its
+// [N, K] transpose, so its blocks of 16 are contiguous too); two codes per byte, element 2i
+// in the low nibble.
+#include "fgq_device.hpp"
+#include "fgq_launch.hpp"
+#include "gemm_common.hpp"
+
+namespace fgq {
+
+// ---------------------------------------------------------------------------------------
+// Quantizer.  The global scale needs the tensor amax before any block can be coded, so a
+// call is four launches on one stream: clear the amax slot, reduce |x| into it (integer max
+// of bf16 magnitude bits, order-independent), code every block, then turn the slot into g.
+// The slot is the caller's global-scale output, used as a uint32 until the last launch.
+// ---------------------------------------------------------------------------------------
+__global__ void nvfp4_clear_kernel(uint32_t* slot)
+{
+    if (threadIdx.x == 0)
+        *slot = 0u;
+}
+
+__global__ __launch_bounds__(256) void nvfp4_amax_kernel(const u32x4* __restrict__ X,
+                                                         int64_t nvec, uint32_t* slot)
+{
+    uint32_t m = 0;
+    for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < nvec;
+         i += (int64_t)gridDim.x * 256)
+        m = max(m, absmax_bits8(__builtin_nontemporal_load(&X[i])));
+    m = wave_max(m);
+    if ((threadIdx.x & 63) == 0)
+        atomicMax(slot, m);
+}
+
+// E2M1 code of y: count the rounding boundaries passed (ties at 0.25, 1.25, 2.5, 5 go down
+// to the even code, ties at 0.75, 1.75, 3.5 go up to it), saturating at 6; sign in bit 3
+__device__ __forceinline__ uint32_t e2m1_code(float y)
+{
+    const float a = __builtin_fabsf(y);
+    const uint32_t c = (uint32_t)(a > 0.25f) + (uint32_t)(a >= 0.75f) + (uint32_t)(a > 1.25f) +
+                       (uint32_t)(a >= 1.75f) + (uint32_t)(a > 2.5f) + (uint32_t)(a >= 3.5f) +
+                       (uint32_t)(a > 5.0f);
+    return c | ((__float_as_uint(y) >> 28) & 8u);
+}
+
+// one lane = 8 consecutive elements (16 bytes) -> 8 codes (4 bytes); a block of 16 is the
+// lane pair (2b, 2b+1), whose amax is exchanged by a DPP quad permute [1,0,3,2]
+__global__ __launch_bounds__(256) void nvfp4_quant_kernel(const u32x4* __restrict__ X,
+                                                          uint32_t* __restrict__ Xq,
+                                                          uint8_t* __restrict__ sX,
+                                                          const uint32_t* __restrict__ slot,
+                                                          int64_t nvec)
+{
+    const float amax_t = __uint_as_float(*slot << 16);
+    const float g = amax_t / 2688.0f;
+    const float six_g = 6.0f * g;
+    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    const u32x4 v = i < nvec ? __builtin_nontemporal_load(&X[i]) : u32x4{0u, 0u, 0u, 0u};
+    uint32_t am = absmax_bits8(v);
+    am = max(am, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)am, 0xB1, 0xF, 0xF, false));
+    uint32_t sb = 0;
+    if (six_g != 0.0f)
+        sb = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(__uint_as_float(am << 16) / six_g, 0.0f,
+                                                      0, false) &
+             0xFFu;
+    const float D = __builtin_amdgcn_cvt_f32_fp8((int)sb, 0) * g;
+    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+    uint32_t packed = 0;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+        const uint32_t b = (e & 1) ? (w[e >> 1] & 0xFFFF0000u) : (w[e >> 1] << 16);
+        const uint32_t c = D == 0.0f ? ((b >> 28) & 8u) : e2m1_code(__uint_as_float(b) / D);
+        packed |= c << (4 * e);
+    }
+    if (i < nvec) {
+        Xq[i] = packed;
+        if ((threadIdx.x & 1) == 0)
+            sX[i >> 1] = (uint8_t)sb;
+    }
+}
+
+__global__ void nvfp4_final_kernel(uint32_t* slot)
+{
+    if (threadIdx.x == 0) {
+        const float amax_t = __uint_as_float(*slot << 16);
+        *reinterpret_cast<float*>(slot) = amax_t / 2688.0f;
+    }
+}
+
+hipError_t launch_quant_nvfp4(const void* X, void* Xq, uint8_t* sX, float* g, int64_t R,
+                              int64_t C, hipStream_t stream)
+{
+    uint32_t* slot = reinterpret_cast<uint32_t*>(g);
+    const int64_t nvec = R * C / 8;
+    hipLaunchKernelGGL(nvfp4_clear_kernel, dim3(1), dim3(64), 0, stream, slot);
+    int64_t ablocks = (nvec + 256 * 8 - 1) / (256 * 8);
+    ablocks = ablocks < 1 ? 1 : (ablocks > 2048 ? 2048 : ablocks);
+    hipLaunchKernelGGL(nvfp4_amax_kernel, dim3((unsigned)ablocks), dim3(256), 0, stream,
+                       static_cast<const u32x4*>(X), nvec, slot);
+    hipLaunchKernelGGL(nvfp4_quant_kernel, dim3((unsigned)((nvec + 255) / 256)), dim3(256), 0,
+                       stream, static_cast<const u32x4*>(X), static_cast<uint32_t*>(Xq), sX,
+                       slot, nvec);
+    hipLaunchKernelGGL(nvfp4_final_kernel, dim3(1), dim3(64), 0, stream, slot);
+    return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------------------
+// GEMM.  C[m,n] = gA*gB * sum_k (e2m1(a[m,k]) * sA[m,k/16]) * (e2m1(b[n,k]) * sB[n,k/16]).
+// Every product e2m1 * E4M3 has at most 6 significant bits and lies in [2^-10, 2688], so the
+// scaled operand is an exact f16; f16 MFMAs sum the products to fp32 accuracy and accumulate
+// straight into the fp32 accumulators over all of K (the block scales are inside the
+// operands, so no per-chunk promotion step is needed); the two global scales multiply the
+// result once.  Operands: v_cvt_scalef32_pk_f16_fp4 with a unit scale (its scale operand is
+// applied as a power of two only, measured) then v_pk_mul_f16 by the block scale.  Both
+// operands are K-contiguous, so every fragment is a plain 16-byte LDS read: lane (q, g)
+// takes 32 consecutive k (bytes 16g..16g+15 of the row's 64-byte chunk), blocks 2g and
+// 2g+1.  The 16-byte chunk of a row is XORed with (row/4)%4 so the 16 rows of a fragment
+// read hit distinct banks.
+// ---------------------------------------------------------------------------------------
+template <int BM_, int BN_, int WM_, int WN_>
+struct Nvfp4Cfg {
+    static constexpr int BM = BM_, BN = BN_, WM = WM_, WN = WN_;
+    static constexpr int NW = WM * WN, NT = 64 * NW;
+    static constexpr int TM = BM / WM, TN = BN / WN, FM = TM / 16, FN = TN / 16;
+    static constexpr int A_BYTES = BM * 64, B_BYTES = BN * 64;
+    static constexpr int SA_BYTES = BM * 8, SB_BYTES = BN * 8;
+    static constexpr int STAGE = A_BYTES + B_BYTES + SA_BYTES + SB_BYTES;
+    static constexpr int A_LOADS = A_BYTES / 1024, B_LOADS = B_BYTES / 1024;
+    static constexpr int SA_LOADS = SA_BYTES / 256, SB_LOADS = SB_BYTES / 256;
+    static_assert(A_LOADS % NW == 0 && B_LOADS % NW == 0, "data loads split evenly");
+    static_assert(2 * STAGE <= 160 * 1024, "LDS capacity");
+    static __device__ __forceinline__ int swz(int row) { return (row >> 2) & 3; }
+};
+
+// block scales of rows r0.. (8 bytes = 8 blocks of 16 per 128-K chunk), two dwords per row,
+// rows past the end repeat the last row
+template <int LOADS, int NW>
+__device__ __forceinline__ void dma_scales(const uint8_t* __restrict__ s, int64_t rows_left,
+                                           int64_t K, int64_t r0, int64_t kb, uint32_t lds,
+                                           int wave, int lane)
+{
+#pragma unroll
+    for (int u = 0; u < (LOADS + NW - 1) / NW; ++u) {
+        const int is = u * NW + wave;
+        if (is < LOADS) {
+            const int idx = is * 64 + lane;
+            int64_t row = idx >> 1;
+            row = row < rows_left ? row : rows_left - 1;
+            dma_b32(s + (r0 + row) * (K / 16) + kb * 8 + (idx & 1) * 4, lds + is * 256);
+        }
+    }
+}
+
+template <class Cfg>
+__device__ __forceinline__ void nvfp4_load(uint8_t LDS* stage, const uint8_t* __restrict__ A,
+                                           const uint8_t* __restrict__ sA,
+                                           const uint8_t* __restrict__ B,
+                                           const uint8_t* __restrict__ sB, int64_t M, int64_t N,
+                                           int64_t K, int64_t m0, int64_t n0, int64_t kb,
+                                           int wave, int lane)
+{
+    // instruction ia covers tile rows 16ia..16ia+15: lane -> row 16ia + lane/4, physical
+    // 16-byte chunk lane%4 holding logical chunk (lane%4) ^ swz(row)
+#pragma unroll
+    for (int u = 0; u < Cfg::A_LOADS / Cfg::NW; ++u) {
+        const int ia = u * Cfg::NW + wave;
+        const int row = ia * 16 + (lane >> 2);
+        const int c = (lane & 3) ^ Cfg::swz(row);
+        int64_t gm = m0 + row;
+        gm = gm < M ? gm : M - 1;
+        dma_b128(A + gm * (K / 2) + kb * 64 + c * 16, lds_addr(stage + ia * 1024));
+    }
+#pragma unroll
+    for (int u = 0; u < Cfg::B_LOADS / Cfg::NW; ++u) {
+        const int ib = u * Cfg::NW + wave;
+        const int row = ib * 16 + (lane >> 2);
+        const int c = (lane & 3) ^ Cfg::swz(row);
+        int64_t gn = n0 + row;
+        gn = gn < N ? gn : N - 1;
+        dma_b128(B + gn * (K / 2) + kb * 64 + c * 16,
+                 lds_addr(stage + Cfg::A_BYTES + ib * 1024));
+    }
+    dma_scales<Cfg::SA_LOADS, Cfg::NW>(sA, M - m0, K, m0, kb,
+                                       lds_addr(stage + Cfg::A_BYTES + Cfg::B_BYTES), wave,
+                                       lane);
+    dma_scales<Cfg::SB_LOADS, Cfg::NW>(
+        sB, N - n0, K, n0, kb, lds_addr(stage + Cfg::A_BYTES + Cfg::B_BYTES + Cfg::SA_BYTES),
+        wave, lane);
+}
+
+// 32 E2M1 codes (16 bytes: k 32g..32g+31) with the E4M3 scales of their two blocks -> the
+// four f16x8 MFMA operands of sub-steps t = 0..3 (sub-step t is bytes 4t..4t+3, block t/2)
+__device__ __forceinline__ void fp4_operands(i32x4 raw, uint32_t scale2, f16x8 (&op)[4])
+{
+    const f16x2 sc = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8((int)scale2, 1.0f, false);
+    const f16x2 s0 = f16x2{sc[0], sc[0]}, s1 = f16x2{sc[1], sc[1]};
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+        const f16x2 s = t < 2 ? s0 : s1;
+        const f16x2 a = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(raw[t], 1.0f, 0) * s;
+        const f16x2 b = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(raw[t], 1.0f, 1) * s;
+        const f16x2 c = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(raw[t], 1.0f, 2) * s;
+        const f16x2 d = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(raw[t], 1.0f, 3) * s;
+        op[t] = f16x8{a[0], a[1], b[0], b[1], c[0], c[1], d[0], d[1]};
+    }
+}
+
+template <class Cfg, bool OUT_BF16>
+__global__ __launch_bounds__(Cfg::NT) void gemm_nvfp4_kernel(
+    const uint8_t* __restrict__ A, const uint8_t* __restrict__ sA, const float* __restrict__ gA,
+    const uint8_t* __restrict__ B, const uint8_t* __restrict__ sB, const float* __restrict__ gB,
+    void* __restrict__ Cout, int64_t M, int64_t N, int64_t K)
+{
+    __shared__ __attribute__((aligned(1024))) uint8_t smem_raw[2 * Cfg::STAGE];
+    uint8_t LDS* const smem = (uint8_t LDS*)smem_raw;
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int wm = wave / Cfg::WN, wn = wave % Cfg::WN;
+    const int g = lane >> 4, q = lane & 15;
+
+    // tiles: XCD-contiguous ranges, walked in groups of 4 tile rows (as the FP8 GEMM)
+    const int64_t tiles_m = (M + Cfg::BM - 1) / Cfg::BM, tiles_n = N / Cfg::BN;
+    const int64_t G = (int64_t)gridDim.x;
+    int64_t pid = blockIdx.x;
+    if (G % 8 == 0)
+        pid = (pid % 8) * (G / 8) + pid / 8;
+    constexpr int GROUP_M = 4;
+    const int64_t first_m = (pid / (GROUP_M * tiles_n)) * GROUP_M;
+    const int64_t gsize = (tiles_m - first_m) < GROUP_M ? (tiles_m - first_m) : GROUP_M;
+    const int64_t m0 = (first_m + pid % gsize) * Cfg::BM;
+    const int64_t n0 = ((pid % (GROUP_M * tiles_n)) / gsize) * Cfg::BN;
+    const int64_t KB = K / 128;
+
+    int a_off[Cfg::FM], sa_off[Cfg::FM], b_off[Cfg::FN], sb_off[Cfg::FN];
+#pragma unroll
+    for (int i = 0; i < Cfg::FM; ++i) {
+        const int row = wm * Cfg::TM + 16 * i + q;
+        a_off[i] = row * 64 + ((g ^ Cfg::swz(row)) * 16);
+        sa_off[i] = Cfg::A_BYTES + Cfg::B_BYTES + row * 8 + 2 * g;
+    }
+#pragma unroll
+    for (int j = 0; j < Cfg::FN; ++j) {
+        const int row = wn * Cfg::TN + 16 * j + q;
+        b_off[j] = Cfg::A_BYTES + row * 64 + ((g ^ Cfg::swz(row)) * 16);
+        sb_off[j] = Cfg::A_BYTES + Cfg::B_BYTES + Cfg::SA_BYTES + row * 8 + 2 * g;
+    }
+
+    f32x4 acc[Cfg::FM][Cfg::FN];
+#pragma unroll
+    for (int i = 0; i < Cfg::FM; ++i)
+#pragma unroll
+        for (int j = 0; j < Cfg::FN; ++j)
+            acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    if (KB > 0)
+        nvfp4_load<Cfg>(smem, A, sA, B, sB, M, N, K, m0, n0, 0, wave, lane);
+    for (int64_t kb = 0; kb < KB; ++kb) {
+        const uint8_t LDS* cur = smem + (kb & 1) * Cfg::STAGE;
+        wait_vm<0>();
+        lds_barrier();   // chunk kb visible to all; chunk kb-1 fully read
+        if (kb + 1 < KB)
+            nvfp4_load<Cfg>(smem + ((kb + 1) & 1) * Cfg::STAGE, A, sA, B, sB, M, N, K, m0, n0,
+                            kb + 1, wave, lane);
+        f16x8 af[Cfg::FM][4];
+#pragma unroll
+        for (int i = 0; i < Cfg::FM; ++i) {
+            const i32x4 raw = *(const i32x4 LDS*)(cur + a_off[i]);
+            const uint32_t s2 = *(const uint16_t LDS*)(cur + sa_off[i]);
+            fp4_operands(raw, s2, af[i]);
+        }
+#pragma unroll
+        for (int j = 0; j < Cfg::FN; ++j) {
+            f16x8 bf[4];
+            const i32x4 raw = *(const i32x4 LDS*)(cur + b_off[j]);
+            const uint32_t s2 = *(const uint16_t LDS*)(cur + sb_off[j]);
+            fp4_operands(raw, s2, bf);
+#pragma unroll
+            for (int t = 0; t < 4; ++t)
+#pragma unroll
+                for (int i = 0; i < Cfg::FM; ++i)
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(af[i][t], bf[t],
+                                                                       acc[i][j], 0, 0, 0);
+        }
+    }
+
+    // lane holds C[16i + 4g + r][16j + q] of the wave tile
+    const float gab = *gA * *gB;
+#pragma unroll
+    for (int i = 0; i < Cfg::FM; ++i)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int64_t row = m0 + wm * Cfg::TM + 16 * i + 4 * g + r;
+            if (row >= M)
+                continue;
+#pragma unroll
+            for (int j = 0; j < Cfg::FN; ++j) {
+                const int64_t col = n0 + wn * Cfg::TN + 16 * j + q;
+                const float v = acc[i][j][r] * gab;
+                if (OUT_BF16)
+                    static_cast<__bf16*>(Cout)[row * N + col] = (__bf16)v;
+                else
+                    static_cast<float*>(Cout)[row * N + col] = v;
+            }
+        }
+}
+
+template <class Cfg>
+static hipError_t launch_nvfp4_cfg(const void* A_q, const uint8_t* sA, const float* gA,
+                                   const void* B_q, const uint8_t* sB, const float* gB, void* C,
+                                   int64_t M, int64_t N, int64_t K, int out_bf16,
+                                   hipStream_t stream)
+{
+    const int64_t tiles = ((M + Cfg::BM - 1) / Cfg::BM) * (N / Cfg::BN);
+    if (out_bf16)
+        hipLaunchKernelGGL((gemm_nvfp4_kernel<Cfg, true>), dim3((unsigned)tiles), dim3(Cfg::NT),
+                           0, stream, static_cast<const uint8_t*>(A_q), sA, gA,
+                           static_cast<const uint8_t*>(B_q), sB, gB, C, M, N, K);
+    else
+        hipLaunchKernelGGL((gemm_nvfp4_kernel<Cfg, false>), dim3((unsigned)tiles), dim3(Cfg::NT),
+                           0, stream, static_cast<const uint8_t*>(A_q), sA, gA,
+                           static_cast<const uint8_t*>(B_q), sB, gB, C, M, N, K);
+    return hipGetLastError();
+}
+
+hipError_t launch_gemm_nvfp4(const void* A_q, const uint8_t* sA, const float* gA,
+                             const void* B_q, const uint8_t* sB, const float* gB, void* C,
+                             int64_t M, int64_t N, int64_t K, int out_bf16, hipStream_t stream)
+{
+    if (M >= 256)
+        return launch_nvfp4_cfg<Nvfp4Cfg<256, 128, 4, 2>>(A_q, sA, gA, B_q, sB, gB, C, M, N, K,
+                                                          out_bf16, stream);
+    return launch_nvfp4_cfg<Nvfp4Cfg<128, 128, 2, 2>>(A_q, sA, gA, B_q, sB, gB, C, M, N, K,
+                                                      out_bf16, stream);
+}
+
+}  // namespace fgq

@@ -156,6 +156,32 @@ int fgq_gemm_fp8_blockscaled_ue8m0(const void* A_q, const uint8_t* scale_A, cons
                                    const uint8_t* scale_B, void* C, int64_t M, int64_t N,
                                    int64_t K, int out_dtype, int variant, void* stream);
 
+/*
+ * NVFP4 two-level scaling (page "Fine-Grained FP8/FP4 Quantization", section "NVFP4
+ * Two-Level Scaling"): E2M1 codes (0, 0.5, 1, 1.5, 2, 3, 4, 6 and signs), one E4M3 scale
+ * per 16 consecutive elements along the contiguous dimension, one fp32 global scale per
+ * tensor; value = global * block * e2m1.  Scales: global = amax/2688 (2688 = 448*6),
+ * block = E4M3(amax_block / (6*global)), code = E2M1(x / (block*global)) nearest-even,
+ * saturating at 6 (signed zeros where block*global is 0).
+ *   X            in : bf16 [R, C] row-major, C % 16 == 0, R*C <= 2^38
+ *   Xq           out: packed codes [R, C/2], element 2i in the low nibble of byte i
+ *   scale_X      out: E4M3 [R, C/16]
+ *   global_scale out: one fp32 (also used as scratch by the call until it completes)
+ * Four launches on `stream` (the tensor amax is needed before any block is coded).
+ */
+int fgq_quantize_nvfp4(const void* X, void* Xq, uint8_t* scale_X, float* global_scale,
+                       int64_t R, int64_t C, void* stream);
+/*
+ * NVFP4 GEMM: C[m,n] = sum_k a[m,k] * b[n,k], a and b dequantized as above.  Both operands
+ * are quantized along K: A_q [M, K/2] with scale_A [M, K/16], and the weight stored as its
+ * transpose B_q [N, K/2] with scale_B [N, K/16]; global_A / global_B are device pointers to
+ * the fp32 global scales.  C fp32 or bf16 [M, N], overwritten.  Requires K % 128 == 0 and
+ * N % 128 == 0; the products are summed to fp32 accuracy (same tolerance as the FP8 GEMM).
+ */
+int fgq_gemm_nvfp4(const void* A_q, const uint8_t* scale_A, const float* global_A,
+                   const void* B_q, const uint8_t* scale_B, const float* global_B, void* C,
+                   int64_t M, int64_t N, int64_t K, int out_dtype, void* stream);
+
 /* Static text for a status code. */
 const char* fgq_status_string(int status);
 

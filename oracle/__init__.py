@@ -227,8 +227,9 @@ def quantize_nvfp4(X_bits: np.ndarray):
     return Xq, sX, np.float32(g[0])
 
 
-def gemm_nvfp4_f64(Aq, sA, gA, Bq, sB, gB, nthreads: int | None = None):
-    """fp64 NVFP4 GEMM reference: (C [M,N], S [M,N]) for A [M,K] and B stored [N,K]."""
+def gemm_nvfp4_f64(Aq, sA, gA, Bq, sB, gB, nthreads: int | None = None, rows=None):
+    """fp64 NVFP4 GEMM reference: (C [M,N], S [M,N]) for A [M,K] and B stored [N,K];
+    rows=(m0, m1) computes only those rows (the others are left as NaN)."""
     lib = _load()
     Aq = np.ascontiguousarray(Aq, dtype=np.uint8)
     Bq = np.ascontiguousarray(Bq, dtype=np.uint8)
@@ -237,12 +238,14 @@ def gemm_nvfp4_f64(Aq, sA, gA, Bq, sB, gB, nthreads: int | None = None):
     M, N, K = Aq.shape[0], Bq.shape[0], Aq.shape[1] * 2
     if Bq.shape[1] * 2 != K or sA.shape != (M, K // 16) or sB.shape != (N, K // 16):
         raise ValueError("shape mismatch")
-    C = np.empty((M, N), dtype=np.float64)
-    S = np.empty((M, N), dtype=np.float64)
+    C = np.full((M, N), np.nan, dtype=np.float64)
+    S = np.full((M, N), np.nan, dtype=np.float64)
+    r0, r1 = rows if rows is not None else (0, M)
     nt = nthreads or threads()
     _run(lambda a, b: lib.oracle_gemm_nvfp4_f64(_ptr(Aq), _ptr(sA), float(gA), _ptr(Bq), _ptr(sB),
-                                                float(gB), M, N, K, _ptr(C), _ptr(S), a, b),
-         _split(M, nt * 4), nt)
+                                                float(gB), M, N, K, _ptr(C), _ptr(S), r0 + a,
+                                                r0 + b),
+         _split(r1 - r0, nt * 4), nt)
     return C, S
 
 

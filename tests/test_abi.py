@@ -133,3 +133,22 @@ def test_gemm_quant_validation(args, want):
 ])
 def test_ue8m0_validation(fn, args, want):
     assert getattr(fgq.load(), fn)(*args, None) == want
+
+
+G1, G2 = 0x80000, 0x90000
+
+
+@pytest.mark.parametrize("fn,args,want", [
+    ("fgq_quantize_nvfp4", (P, Q, R, G1, 4, 24), -2),          # C % 16
+    ("fgq_quantize_nvfp4", (P, Q, R, None, 4, 32), -1),
+    ("fgq_quantize_nvfp4", (P, Q, R, G1 + 4, 4, 32), -3),
+    ("fgq_quantize_nvfp4", (P, Q, R, P + 16, 4, 32), -6),      # global scale inside X
+    ("fgq_quantize_nvfp4", (None, None, None, None, 0, 32), 0),
+    ("fgq_gemm_nvfp4", (P, S1, G1, Q, S2, G2, R, 4, 128, 100, 0), -2),   # K % 128
+    ("fgq_gemm_nvfp4", (P, S1, G1, Q, S2, G2, R, 4, 128, 128, 3), -4),
+    ("fgq_gemm_nvfp4", (P, S1, None, Q, S2, G2, R, 4, 128, 128, 0), -1),
+    ("fgq_gemm_nvfp4", (P, S1, G1, Q, S2, G2, G1 - 16, 4, 128, 128, 0), -6),
+    ("fgq_gemm_nvfp4", (None,) * 7 + (0, 128, 128, 0), 0),
+])
+def test_nvfp4_validation(fn, args, want):
+    assert getattr(fgq.load(), fn)(*args, None) == want
