@@ -38,7 +38,9 @@ def log(msg):
 
 PROFILES = os.path.join(ROOT, "profiles")
 KERNEL_SOURCES = {   # the sources each profiled kernel is built from (for staleness checks)
-    "gemm": ["fine_grained_block_fgq_amd/csrc/gemm.hip"],
+    "gemm": ["fine_grained_block_fgq_amd/csrc/gemm.hip",
+             "fine_grained_block_fgq_amd/csrc/gemm_common.hpp",
+             "fine_grained_block_fgq_amd/csrc/fgq_device.hpp"],
     "quant_act": ["fine_grained_block_fgq_amd/csrc/quant.hip",
                   "fine_grained_block_fgq_amd/csrc/fgq_device.hpp"],
 }

@@ -26,16 +26,33 @@ __global__ void nvfp4_clear_kernel(uint32_t* slot)
         *slot = 0u;
 }
 
+// grid-stride max with four loads in flight per lane, reduced over the workgroup in LDS:
+// one atomic per workgroup (at most NVFP4_AMAX_BLOCKS of them on the one address)
+constexpr int NVFP4_AMAX_BLOCKS = 512;
+
 __global__ __launch_bounds__(256) void nvfp4_amax_kernel(const u32x4* __restrict__ X,
                                                          int64_t nvec, uint32_t* slot)
 {
+    __shared__ uint32_t wave_amax[4];
     uint32_t m = 0;
-    for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < nvec;
-         i += (int64_t)gridDim.x * 256)
+    const int64_t stride = (int64_t)gridDim.x * 256;
+    int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    for (; i + 3 * stride < nvec; i += 4 * stride) {
+        const u32x4 a = __builtin_nontemporal_load(&X[i]);
+        const u32x4 b = __builtin_nontemporal_load(&X[i + stride]);
+        const u32x4 c = __builtin_nontemporal_load(&X[i + 2 * stride]);
+        const u32x4 d = __builtin_nontemporal_load(&X[i + 3 * stride]);
+        m = max(max(m, max(absmax_bits8(a), absmax_bits8(b))),
+                max(absmax_bits8(c), absmax_bits8(d)));
+    }
+    for (; i < nvec; i += stride)
         m = max(m, absmax_bits8(__builtin_nontemporal_load(&X[i])));
     m = wave_max(m);
     if ((threadIdx.x & 63) == 0)
-        atomicMax(slot, m);
+        wave_amax[threadIdx.x >> 6] = m;
+    __syncthreads();
+    if (threadIdx.x == 0)
+        atomicMax(slot, max(max(wave_amax[0], wave_amax[1]), max(wave_amax[2], wave_amax[3])));
 }
 
 // E2M1 code of y: count the rounding boundaries passed (ties at 0.25, 1.25, 2.5, 5 go down
@@ -99,8 +116,8 @@ hipError_t launch_quant_nvfp4(const void* X, void* Xq, uint8_t* sX, float* g, in
     uint32_t* slot = reinterpret_cast<uint32_t*>(g);
     const int64_t nvec = R * C / 8;
     hipLaunchKernelGGL(nvfp4_clear_kernel, dim3(1), dim3(64), 0, stream, slot);
-    int64_t ablocks = (nvec + 256 * 8 - 1) / (256 * 8);
-    ablocks = ablocks < 1 ? 1 : (ablocks > 2048 ? 2048 : ablocks);
+    int64_t ablocks = (nvec + 256 * 16 - 1) / (256 * 16);
+    ablocks = ablocks < 1 ? 1 : (ablocks > NVFP4_AMAX_BLOCKS ? NVFP4_AMAX_BLOCKS : ablocks);
     hipLaunchKernelGGL(nvfp4_amax_kernel, dim3((unsigned)ablocks), dim3(256), 0, stream,
                        static_cast<const u32x4*>(X), nvec, slot);
     hipLaunchKernelGGL(nvfp4_quant_kernel, dim3((unsigned)((nvec + 255) / 256)), dim3(256), 0,
