@@ -15,7 +15,13 @@ hipError_t launch_quant_act_1x128_ue8m0(const void* X, void* Xq, uint8_t* sX, in
 hipError_t launch_quant_weight_128x128_ue8m0(const void* W, void* Wq, uint8_t* sW, int64_t K,
                                              int64_t N, hipStream_t stream);
 // GEMM kernel families (values of fgq_gemm_variant)
-enum GemmVariant { GEMM_AUTO = 0, GEMM_WIDE_256x128 = 1, GEMM_WIDE_128x128 = 2, GEMM_NARROW = 3 };
+enum GemmVariant {
+    GEMM_AUTO = 0,
+    GEMM_WIDE_256x128 = 1,
+    GEMM_WIDE_128x128 = 2,
+    GEMM_NARROW = 3,
+    GEMM_SKINNY = 4
+};
 
 // out_bf16: 0 -> C is fp32, 1 -> C is bf16 (nearest-even)
 hipError_t launch_gemm_fp8_blockscaled(const void* A_q, const float* sA, const void* B_q,

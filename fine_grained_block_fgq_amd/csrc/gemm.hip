@@ -58,10 +58,10 @@ struct GemmCfg {
     static constexpr int B_ROWS_PER_LOAD = 1024 / BN;
     static constexpr int B_CHUNKS = BN / 16;
     static_assert(TN <= 128 && 128 % TN == 0, "a wave's columns must sit in one 128-block");
-    static_assert(TM % 16 == 0 && TN % 16 == 0 && BN >= 128 && BM % 64 == 0, "tile shape");
+    static_assert(TM % 16 == 0 && TN % 16 == 0 && BN >= 32 && BM % 64 == 0, "tile shape");
     static_assert(A_LOADS % NW == 0 && B_LOADS % NW == 0, "loads split evenly over waves");
     static_assert(S_LOADS <= NW, "one scale load per wave at most");
-    static_assert(STAGES == 2 || STAGES == 3, "LDS ring depth");
+    static_assert(STAGES >= 2 && STAGES <= 4, "LDS ring depth");
     static_assert(STAGES * STAGE <= 160 * 1024, "LDS capacity (160 KB per CU)");
     // 16-byte column swizzles.  gfx950 LDS has 64 banks of 4 bytes (256 B per cycle): a
     // ds_read_b128 serves 16 lanes per cycle, a ds_read_b64(_tr) 32 lanes.  A rows are 128 B
@@ -80,13 +80,17 @@ struct GemmCfg {
     static __device__ __forceinline__ int b_swz(int k)
     {
 #if FGQ_SWZ
+        // BN = 32: rows are two 16-byte chunks; the 8 rows of one transposed read already
+        // cover 32 banks, and bit 5 of k separates the two groups read in the same cycle
+        if (B_CHUNKS == 2)
+            return (k >> 5) & 1;
         return B_CHUNKS == 8 ? (((k >> 1) & 3) | (((k >> 5) & 1) << 2))
                              : ((k & 7) | (((k >> 5) & 1) << 3));
 #else
         return k & 7;
 #endif
     }
-    static_assert(B_CHUNKS == 8 || B_CHUNKS == 16, "BN is 128 or 256");
+    static_assert(B_CHUNKS == 2 || B_CHUNKS == 8 || B_CHUNKS == 16, "BN is 32, 128 or 256");
     // waits: every wave issues this many direct-to-LDS loads per stage (S loads go to the
     // first S_LOADS waves); the pipeline waits with the smallest count, which is safe.
     static constexpr int MIN_LOADS = (A_LOADS + B_LOADS) / NW;
@@ -364,7 +368,11 @@ __global__ __launch_bounds__(Cfg::NT) void gemm_fp8_blockscaled_kernel(
     for (int64_t kb = 0; kb < KB; ++kb) {
         const uint8_t LDS* cur = smem + (kb % Cfg::STAGES) * Cfg::STAGE;
         // chunk kb has landed once only the later chunks' loads may still be outstanding
-        if (Cfg::STAGES == 3 && kb + 1 < KB)
+        // (chunks kb+1 .. kb+STAGES-2, those already issued)
+        const int64_t later = (KB - 1 - kb) < (Cfg::STAGES - 2) ? (KB - 1 - kb) : (Cfg::STAGES - 2);
+        if (Cfg::STAGES >= 4 && later >= 2)
+            wait_vm<2 * Cfg::MIN_LOADS>();
+        else if (Cfg::STAGES >= 3 && later >= 1)
             wait_vm<Cfg::MIN_LOADS>();
         else
             wait_vm<0>();
@@ -382,7 +390,8 @@ __global__ __launch_bounds__(Cfg::NT) void gemm_fp8_blockscaled_kernel(
             lds_barrier();   // chunk kb fully read before the next iteration refills it
     }
 
-    if (FUSE || (OUT_BF16 && FGQ_STAGED_STORE)) {
+    static_assert(!FUSE || Cfg::BN >= 128, "the fused epilogue needs whole 128-column groups");
+    if constexpr (FUSE || (OUT_BF16 && FGQ_STAGED_STORE && Cfg::BN >= 128)) {
         // bf16 C leaves through an LDS-staged tile: 16-byte row-contiguous stores (and, fused,
         // the quantization of every row group)
         lds_barrier();   // every wave is done with the ring: it becomes the staging tile
@@ -433,6 +442,165 @@ static hipError_t launch_cfg(const void* A_q, const void* sA_, const void* B_q, 
         hipLaunchKernelGGL((gemm_fp8_blockscaled_kernel<Cfg, SI, false>), dim3((unsigned)tiles),
                            dim3(Cfg::NT), 0, stream, static_cast<const uint8_t*>(A_q), sA,
                            static_cast<const uint8_t*>(B_q), sB, C, M, N, K, n_begin, n_end);
+    return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------------------
+// Skinny shapes (M <= 128, decode-like): one workgroup per BM x 32 output tile with its K
+// chunks split over KG groups of NW waves.  Group c takes chunks c, c+KG, ...: a ring stage
+// holds KG chunks side by side, each loaded and computed by its own group with the wide
+// kernel's per-chunk code, so two waves share each SIMD (latency hiding) while the A/B
+// stages stay within LDS.  The KG partial tiles are summed in LDS in group order (fixed:
+// results are repeatable bit for bit) and stored by group 0.
+template <class Cfg, class SI, bool OUT_BF16, int KG>
+__global__ __launch_bounds__(Cfg::NT * KG) void gemm_fp8_blockscaled_ksplit_kernel(
+    const uint8_t* __restrict__ A, const typename SI::T* __restrict__ sA,
+    const uint8_t* __restrict__ B, const typename SI::T* __restrict__ sB,
+    void* __restrict__ Cout, int64_t M, int64_t N, int64_t K)
+{
+    static_assert(Cfg::WN * Cfg::TN == Cfg::BN && Cfg::BN <= 128, "skinny tile");
+    constexpr int RING = Cfg::STAGES * KG * Cfg::STAGE;
+    constexpr int RED = (KG - 1) * Cfg::NT * Cfg::FM * Cfg::FN * 16;
+    __shared__ __attribute__((aligned(1024))) uint8_t smem_raw[RING > RED ? RING : RED];
+    uint8_t LDS* const smem = (uint8_t LDS*)smem_raw;
+
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int kg = wave / Cfg::NW, wl = wave % Cfg::NW;   // K group, wave within the group
+    const int wm = wl / Cfg::WN, wn = wl % Cfg::WN;
+    const int g = lane >> 4, q = lane & 15;
+
+    // tiles: row tiles fastest; XCD-contiguous ranges (ids are dealt round-robin to XCDs)
+    const int64_t tiles_m = (M + Cfg::BM - 1) / Cfg::BM;
+    const int64_t G = (int64_t)gridDim.x;
+    int64_t pid = blockIdx.x;
+    if (G % 8 == 0)
+        pid = (pid % 8) * (G / 8) + pid / 8;
+    const int64_t m0 = (pid % tiles_m) * Cfg::BM, n0 = (pid / tiles_m) * Cfg::BN;
+    const int64_t KB = K / 128, NB = N / 128;
+    const int64_t steps = (KB + KG - 1) / KG;
+
+    int a_off[Cfg::FM][2];
+#pragma unroll
+    for (int i = 0; i < Cfg::FM; ++i) {
+        const int row = wm * Cfg::TM + 16 * i + q;
+        a_off[i][0] = row * 128 + (((2 * g) ^ Cfg::a_swz(row)) * 16);
+        a_off[i][1] = row * 128 + (((2 * g + 1) ^ Cfg::a_swz(row)) * 16);
+    }
+    int b_off[Cfg::FN][4];
+#pragma unroll
+    for (int j = 0; j < Cfg::FN; ++j) {
+        const int ch = (wn * Cfg::TN + 16 * j) / 16;
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+            const int k = 32 * g + 8 * t + (q >> 1);
+            b_off[j][t] = Cfg::A_BYTES + k * Cfg::BN + ((ch ^ Cfg::b_swz(k)) * 16) + 8 * (q & 1);
+        }
+    }
+    const int s_off = Cfg::A_BYTES + Cfg::B_BYTES + (wm * Cfg::TM + 4 * g) * 4;
+    const int64_t nb = (n0 + wn * Cfg::TN) / 128;
+
+    f32x4 acc[Cfg::FM][Cfg::FN];
+#pragma unroll
+    for (int i = 0; i < Cfg::FM; ++i)
+#pragma unroll
+        for (int j = 0; j < Cfg::FN; ++j)
+            acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    // this group's chunk of step s is kb = s*KG + kg (if < KB)
+    auto stage_of = [&](int64_t st) { return smem + ((st % Cfg::STAGES) * KG + kg) * Cfg::STAGE; };
+#pragma unroll
+    for (int st = 0; st < Cfg::STAGES - 1; ++st)
+        if (st < steps && st * KG + kg < KB)
+            load_stage<Cfg, SI>(stage_of(st), A, sA, B, M, N, K, m0, n0, st * KG + kg, wl, lane);
+
+    for (int64_t st = 0; st < steps; ++st) {
+        const int64_t kb = st * KG + kg;
+        // this wave's own loads issued for later steps (chunk present in those steps)
+        int later = 0;
+#pragma unroll
+        for (int d = 1; d <= Cfg::STAGES - 2; ++d)
+            later += (st + d < steps && (st + d) * KG + kg < KB) ? 1 : 0;
+        if (Cfg::STAGES >= 4 && later >= 2)
+            wait_vm<2 * Cfg::MIN_LOADS>();
+        else if (Cfg::STAGES >= 3 && later >= 1)
+            wait_vm<Cfg::MIN_LOADS>();
+        else
+            wait_vm<0>();
+        lds_barrier();   // step st visible to all; step st-1 fully read (its stage refills)
+        const int64_t nxt = st + Cfg::STAGES - 1;
+        if (nxt < steps && nxt * KG + kg < KB)
+            load_stage<Cfg, SI>(stage_of(nxt), A, sA, B, M, N, K, m0, n0, nxt * KG + kg, wl,
+                                lane);
+        if (kb < KB) {
+            const float sb = SI::value(sB[kb * NB + nb]);
+            compute_chunk<Cfg, SI>(stage_of(st), a_off, b_off, s_off, sb, acc);
+        }
+        if (Cfg::STAGES == 2)
+            lds_barrier();
+    }
+
+    // sum the KG partial tiles in group order
+    lds_barrier();
+    float LDS* const red = (float LDS*)smem_raw;
+    constexpr int PER_LANE = Cfg::FM * Cfg::FN * 4;
+    if (kg > 0) {
+#pragma unroll
+        for (int i = 0; i < Cfg::FM; ++i)
+#pragma unroll
+            for (int j = 0; j < Cfg::FN; ++j)
+                *(f32x4 LDS*)(red + (((kg - 1) * Cfg::NT + wl * 64 + lane) * PER_LANE +
+                                     (i * Cfg::FN + j) * 4)) = acc[i][j];
+    }
+    lds_barrier();
+    if (kg != 0)
+        return;
+#pragma unroll
+    for (int c = 1; c < KG; ++c)
+#pragma unroll
+        for (int i = 0; i < Cfg::FM; ++i)
+#pragma unroll
+            for (int j = 0; j < Cfg::FN; ++j)
+                acc[i][j] += *(const f32x4 LDS*)(red + (((c - 1) * Cfg::NT + wl * 64 + lane) *
+                                                            PER_LANE +
+                                                        (i * Cfg::FN + j) * 4));
+    // lane holds C[16i + 4g + r][16j + q] of the wave tile
+#pragma unroll
+    for (int i = 0; i < Cfg::FM; ++i)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int64_t row = m0 + wm * Cfg::TM + 16 * i + 4 * g + r;
+            if (row >= M)
+                continue;
+#pragma unroll
+            for (int j = 0; j < Cfg::FN; ++j) {
+                const int64_t col = n0 + wn * Cfg::TN + 16 * j + q;
+                if (OUT_BF16)
+                    static_cast<__bf16*>(Cout)[row * N + col] = (__bf16)acc[i][j][r];
+                else
+                    static_cast<float*>(Cout)[row * N + col] = acc[i][j][r];
+            }
+        }
+}
+
+template <class Cfg, class SI, int KG>
+static hipError_t launch_ksplit(const void* A_q, const void* sA_, const void* B_q,
+                                const void* sB_, void* C, int64_t M, int64_t N, int64_t K,
+                                int out_bf16, hipStream_t stream)
+{
+    const typename SI::T* sA = static_cast<const typename SI::T*>(sA_);
+    const typename SI::T* sB = static_cast<const typename SI::T*>(sB_);
+    const int64_t tiles = ((M + Cfg::BM - 1) / Cfg::BM) * (N / Cfg::BN);
+    if (out_bf16)
+        hipLaunchKernelGGL((gemm_fp8_blockscaled_ksplit_kernel<Cfg, SI, true, KG>),
+                           dim3((unsigned)tiles), dim3(Cfg::NT * KG), 0, stream,
+                           static_cast<const uint8_t*>(A_q), sA,
+                           static_cast<const uint8_t*>(B_q), sB, C, M, N, K);
+    else
+        hipLaunchKernelGGL((gemm_fp8_blockscaled_ksplit_kernel<Cfg, SI, false, KG>),
+                           dim3((unsigned)tiles), dim3(Cfg::NT * KG), 0, stream,
+                           static_cast<const uint8_t*>(A_q), sA,
+                           static_cast<const uint8_t*>(B_q), sB, C, M, N, K);
     return hipGetLastError();
 }
 
@@ -647,6 +815,13 @@ using CfgSmall = GemmCfg<FGQ_SMALL_CFG>;
 #define FGQ_NARROW_CFG 64, 4, 2
 #endif
 using CfgNarrow = NarrowCfg<FGQ_NARROW_CFG>;
+#ifndef FGQ_SKINNY_CFG
+#define FGQ_SKINNY_CFG 128, 32, 4, 1, 3
+#endif
+#ifndef FGQ_SKINNY_KG
+#define FGQ_SKINNY_KG 2
+#endif
+using CfgSkinny = GemmCfg<FGQ_SKINNY_CFG>;
 
 // compute units of the current device (queried once per device)
 static int device_cus()
@@ -707,6 +882,7 @@ static hipError_t launch_gemm(const void* A_q, const void* sA, const void* B_q, 
         const int64_t tiles_small = ((M + CfgSmall::BM - 1) / CfgSmall::BM) * (N / CfgSmall::BN);
         variant = (M >= 256 && tiles_large >= 256) ? GEMM_WIDE_256x128
                   : tiles_small >= 256             ? GEMM_WIDE_128x128
+                  : M <= 128                       ? GEMM_SKINNY
                                                    : GEMM_NARROW;
     }
     switch (variant) {
@@ -716,6 +892,9 @@ static hipError_t launch_gemm(const void* A_q, const void* sA, const void* B_q, 
         return launch_cfg<CfgSmall, SI>(A_q, sA, B_q, sB, C, M, N, K, out_bf16, stream);
     case GEMM_NARROW:
         return launch_narrow<CfgNarrow, SI>(A_q, sA, B_q, sB, C, M, N, K, out_bf16, stream);
+    case GEMM_SKINNY:
+        return launch_ksplit<CfgSkinny, SI, FGQ_SKINNY_KG>(A_q, sA, B_q, sB, C, M, N, K, out_bf16,
+                                                           stream);
     default:
         return hipErrorInvalidValue;
     }
