@@ -41,12 +41,18 @@
 #ifndef FGQ_STAGED_STORE
 #define FGQ_STAGED_STORE 1
 #endif
+#ifndef FGQ_SPREAD_DMA
+#define FGQ_SPREAD_DMA 1
+#endif
 
 namespace fgq {
 
-template <int BM_, int BN_, int WM_, int WN_, int STAGES_>
+template <int BM_, int BN_, int WM_, int WN_, int STAGES_, bool PP_ = false>
 struct GemmCfg {
     static constexpr int BM = BM_, BN = BN_, WM = WM_, WN = WN_, STAGES = STAGES_;
+    // PP: the second half of the waves (one per SIMD) runs half a chunk behind the first
+    // (see the wide kernel's main loop); needs a 3-stage ring
+    static constexpr bool PP = PP_;
     static constexpr int NW = WM * WN, NT = 64 * NW;
     static constexpr int TM = BM / WM, TN = BN / WN;
     static constexpr int FM = TM / 16, FN = TN / 16;
@@ -62,6 +68,7 @@ struct GemmCfg {
     static_assert(A_LOADS % NW == 0 && B_LOADS % NW == 0, "loads split evenly over waves");
     static_assert(S_LOADS <= NW, "one scale load per wave at most");
     static_assert(STAGES >= 2 && STAGES <= 4, "LDS ring depth");
+    static_assert(!PP || (STAGES == 3 && NW == 8 && FN % 2 == 0), "ping-pong: 3 stages, 8 waves");
     static_assert(STAGES * STAGE <= 160 * 1024, "LDS capacity (160 KB per CU)");
     // 16-byte column swizzles.  gfx950 LDS has 64 banks of 4 bytes (256 B per cycle): a
     // ds_read_b128 serves 16 lanes per cycle, a ds_read_b64(_tr) 32 lanes.  A rows are 128 B
@@ -169,51 +176,125 @@ __device__ __forceinline__ void load_stage(uint8_t LDS* stage, const uint8_t* __
     }
 }
 
-// One 128-K chunk of the wave's 16x16 tiles: f16 operands, four chained f16 MFMAs per
-// tile, then acc += P * (sA*sB).
+// The wave's direct-to-LDS loads of one stage as separately issued pieces (A loads, then B
+// loads, then the scale load), so that a chunk's refill can be spread over the column
+// blocks of the previous chunk's compute: issued all at once right after a barrier, the 56
+// loads of the eight waves queue at the CU's address unit (about 1 KB per 16 cycles) and
+// hold every wave for hundreds of cycles while its SIMD's matrix core idles.
+#ifndef FGQ_DMA_WAVES
+#define FGQ_DMA_WAVES 0
+#endif
 template <class Cfg, class SI>
-__device__ __forceinline__ void compute_chunk(const uint8_t LDS* cur, const int (&a_off)[Cfg::FM][2],
-                                              const int (&b_off)[Cfg::FN][4], int s_off, float sb,
-                                              f32x4 (&acc)[Cfg::FM][Cfg::FN])
-{
-    // combined scales for this lane's rows: sA[row, kb] * sB[kb, nb]
-    f32x4 cs[Cfg::FM];
-#pragma unroll
-    for (int i = 0; i < Cfg::FM; ++i) {
-        cs[i] = SI::combine(cur + s_off + i * 64, sb);
+struct StageLoader {
+    // loading waves: all, or (FGQ_DMA_WAVES) only the first ones -- one per SIMD, the waves
+    // that the SIMD's arbiter favours, so that the issue stalls fall on them
+    static constexpr int LW = (FGQ_DMA_WAVES > 0 && FGQ_DMA_WAVES < Cfg::NW) ? FGQ_DMA_WAVES : Cfg::NW;
+    static_assert(Cfg::A_LOADS % LW == 0 && Cfg::B_LOADS % LW == 0 && Cfg::S_LOADS <= LW,
+                  "loads split evenly over the loading waves");
+    static constexpr int NA = Cfg::A_LOADS / LW, NBL = Cfg::B_LOADS / LW;
+    static constexpr int PIECES = NA + NBL + 1;
+    // pieces per column block, over the first FN-1 blocks (the last block issues none, so
+    // the last piece still has most of a chunk to land)
+    static constexpr int PER = Cfg::FN > 1 ? (PIECES + Cfg::FN - 2) / (Cfg::FN - 1) : PIECES;
+    uint8_t LDS* stage;
+    const uint8_t* __restrict__ A;
+    const typename SI::T* __restrict__ sA;
+    const uint8_t* __restrict__ B;
+    int64_t M, N, K, m0, n0, kb;
+    int wave, lane;
+    bool active;
+
+    __device__ __forceinline__ void piece(int pc) const
+    {
+        if (pc < NA) {
+            const int ia = pc * LW + wave;
+            const int row = ia * 8 + (lane >> 3);
+            const int c = (lane & 7) ^ Cfg::a_swz(row);
+            int64_t gm = m0 + row;
+            gm = gm < M ? gm : M - 1;
+            dma_b128(A + gm * K + kb * 128 + c * 16, lds_addr(stage + ia * 1024));
+        } else if (pc < NA + NBL) {
+            const int ib = (pc - NA) * LW + wave;
+            const int k = ib * Cfg::B_ROWS_PER_LOAD + lane / Cfg::B_CHUNKS;
+            const int q = lane % Cfg::B_CHUNKS;
+            const int c = q ^ Cfg::b_swz(k);
+            int64_t gn = n0 + c * 16;
+            gn = gn < N ? gn : N - 16;
+            dma_b128(B + (kb * 128 + k) * N + gn, lds_addr(stage + Cfg::A_BYTES + ib * 1024));
+        } else if (wave < Cfg::S_LOADS) {
+            int64_t gm = m0 + wave * 64 + lane;
+            gm = gm < M ? gm : M - 1;
+            SI::dma(sA + gm * (K / 128) + kb,
+                    lds_addr(stage + Cfg::A_BYTES + Cfg::B_BYTES + wave * 256));
+        }
     }
-    // A operands: lane bytes 8t..8t+7 of its 32 (k = 32g + 8t + b) -> sub-step t
-    i32x4 araw[Cfg::FM][2];
+    // the pieces that go out just before column block j
+    __device__ __forceinline__ void before_block(int j) const
+    {
+        if (!active || wave >= LW)
+            return;
 #pragma unroll
-    for (int i = 0; i < Cfg::FM; ++i) {
-        araw[i][0] = *(const i32x4 LDS*)(cur + a_off[i][0]);
-        araw[i][1] = *(const i32x4 LDS*)(cur + a_off[i][1]);
+        for (int pc = j * PER; pc < (j + 1) * PER && pc < PIECES; ++pc)
+            piece(pc);
+    }
+};
+
+// loader that issues nothing (the chunk's refill went out elsewhere)
+struct NoLoader {
+    __device__ __forceinline__ void before_block(int) const {}
+};
+
+// Part of one 128-K chunk of the wave's 16x16 tiles: the column blocks [J0, J1).  FIRST
+// parts also read the chunk's combined scales and convert the wave's A operands (both kept
+// in registers for the chunk's later parts).  Per tile: f16 operands, four chained f16
+// MFMAs, then acc += P * (sA*sB).
+template <class Cfg, class SI, int J0, int J1, bool FIRST, class Loader = NoLoader>
+__device__ __forceinline__ void compute_part(const uint8_t LDS* cur, const int (&a_off)[Cfg::FM][2],
+                                             const int (&b_off)[Cfg::FN][4], int s_off, float sb,
+                                             f16x8 (&af)[Cfg::FM][4], f32x4 (&cs)[Cfg::FM],
+                                             f32x4 (&acc)[Cfg::FM][Cfg::FN],
+                                             const Loader& loader = Loader())
+{
+    i32x4 araw[Cfg::FM][2];
+    if constexpr (FIRST) {
+        // combined scales for this lane's rows: sA[row, kb] * sB[kb, nb]
+#pragma unroll
+        for (int i = 0; i < Cfg::FM; ++i)
+            cs[i] = SI::combine(cur + s_off + i * 64, sb);
+        // A operands: lane bytes 8t..8t+7 of its 32 (k = 32g + 8t + b) -> sub-step t
+#pragma unroll
+        for (int i = 0; i < Cfg::FM; ++i) {
+            araw[i][0] = *(const i32x4 LDS*)(cur + a_off[i][0]);
+            araw[i][1] = *(const i32x4 LDS*)(cur + a_off[i][1]);
+        }
     }
     // B operands: transposed read t gives k = 32g + 8t + b for column q -> sub-step t
     i32x2 braw[2][4];
 #pragma unroll
     for (int t = 0; t < 4; ++t)
-        braw[0][t] = __builtin_amdgcn_ds_read_tr8_b64_v2i32((i32x2 LDS*)(cur + b_off[0][t]));
-    f16x8 af[Cfg::FM][4];
+        braw[0][t] = __builtin_amdgcn_ds_read_tr8_b64_v2i32((i32x2 LDS*)(cur + b_off[J0][t]));
+    if constexpr (FIRST) {
 #pragma unroll
-    for (int i = 0; i < Cfg::FM; ++i) {
-        af[i][0] = e4m3x8_to_f16(araw[i][0][0], araw[i][0][1]);
-        af[i][1] = e4m3x8_to_f16(araw[i][0][2], araw[i][0][3]);
-        af[i][2] = e4m3x8_to_f16(araw[i][1][0], araw[i][1][1]);
-        af[i][3] = e4m3x8_to_f16(araw[i][1][2], araw[i][1][3]);
+        for (int i = 0; i < Cfg::FM; ++i) {
+            af[i][0] = e4m3x8_to_f16(araw[i][0][0], araw[i][0][1]);
+            af[i][1] = e4m3x8_to_f16(araw[i][0][2], araw[i][0][3]);
+            af[i][2] = e4m3x8_to_f16(araw[i][1][0], araw[i][1][1]);
+            af[i][3] = e4m3x8_to_f16(araw[i][1][2], araw[i][1][3]);
+        }
     }
 #pragma unroll
-    for (int j = 0; j < Cfg::FN; ++j) {
-        if (j + 1 < Cfg::FN) {
+    for (int j = J0; j < J1; ++j) {
+        loader.before_block(j);
+        if (j + 1 < J1) {
 #pragma unroll
             for (int t = 0; t < 4; ++t)
-                braw[(j + 1) & 1][t] =
+                braw[(j + 1 - J0) & 1][t] =
                     __builtin_amdgcn_ds_read_tr8_b64_v2i32((i32x2 LDS*)(cur + b_off[j + 1][t]));
         }
         f16x8 bf[4];
 #pragma unroll
         for (int t = 0; t < 4; ++t)
-            bf[t] = e4m3x8_to_f16(braw[j & 1][t][0], braw[j & 1][t][1]);
+            bf[t] = e4m3x8_to_f16(braw[(j - J0) & 1][t][0], braw[(j - J0) & 1][t][1]);
         f32x4 p[Cfg::FM];
 #pragma unroll
         for (int i = 0; i < Cfg::FM; ++i)
@@ -230,6 +311,18 @@ __device__ __forceinline__ void compute_chunk(const uint8_t LDS* cur, const int 
             for (int r = 0; r < 4; ++r)
                 acc[i][j][r] = __builtin_fmaf(p[i][r], cs[i][r], acc[i][j][r]);
     }
+}
+
+// One whole 128-K chunk (and, with a StageLoader, the refill of another stage).
+template <class Cfg, class SI, class Loader = NoLoader>
+__device__ __forceinline__ void compute_chunk(const uint8_t LDS* cur, const int (&a_off)[Cfg::FM][2],
+                                              const int (&b_off)[Cfg::FN][4], int s_off, float sb,
+                                              f32x4 (&acc)[Cfg::FM][Cfg::FN],
+                                              const Loader& loader = Loader())
+{
+    f16x8 af[Cfg::FM][4];
+    f32x4 cs[Cfg::FM];
+    compute_part<Cfg, SI, 0, Cfg::FN, true>(cur, a_off, b_off, s_off, sb, af, cs, acc, loader);
 #if FGQ_SCHED == 1
     __builtin_amdgcn_iglp_opt(0);
 #elif FGQ_SCHED == 2
@@ -355,16 +448,57 @@ __global__ __launch_bounds__(Cfg::NT) void gemm_fp8_blockscaled_kernel(
         for (int j = 0; j < Cfg::FN; ++j)
             acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
+    // scale_B of the wave's column block, loaded one chunk ahead: the scalar load then
+    // completes under the LDS barrier's wait instead of stalling the chunk's LDS reads
+    const typename SI::T* const sB_col = sB + (nb_wave < NB ? nb_wave : NB - 1);
+    float sb_next = KB > 0 ? SI::value(sB_col[0]) : 0.0f;
+
+    if constexpr (Cfg::PP) {
+        // Ping-pong schedule.  Every wave computes chunk after chunk, each chunk as a first
+        // half (scales, A operands, column blocks 0..FN/2-1) then a second half; barrier k
+        // (chunk k landed everywhere; chunk k+1's loads then go out) comes before chunk k's
+        // first half in the leading waves (0..3, one per SIMD) and before chunk k-1's second
+        // half in the lagging waves (4..7).  So on every SIMD one wave is in the MFMA-heavy
+        // middle of a chunk while the other reads and converts the start of one.  Between
+        // barriers k and k+1 chunks k-1 and k are read, so slot (k+1) % 3, last read before
+        // barrier k, takes chunk k+1.
+        const bool lag = wave >= Cfg::NW / 2;
+        int slot = 0;   // ring slot of chunk c
+        auto sync_and_load = [&](int64_t k) {   // barrier k
+            wait_vm<0>();    // this wave's loads of chunk k have landed
+            lds_barrier();   // ... everyone's
+            if (k + 1 < KB)
+                load_stage<Cfg, SI>(smem + ((k + 1) % 3) * Cfg::STAGE, A, sA, B, M, N, K, m0, n0,
+                                    k + 1, wave, lane);
+        };
+        if (KB > 0)
+            load_stage<Cfg, SI>(smem, A, sA, B, M, N, K, m0, n0, 0, wave, lane);
+        sync_and_load(0);
+        for (int64_t c = 0; c < KB; ++c) {
+            if (!lag && c > 0)
+                sync_and_load(c);
+            const float sb = sb_next;
+            if (c + 1 < KB)
+                sb_next = SI::value(sB_col[(c + 1) * NB]);
+            const uint8_t LDS* cur = smem + slot * Cfg::STAGE;
+            f16x8 af[Cfg::FM][4];
+            f32x4 cs[Cfg::FM];
+            compute_part<Cfg, SI, 0, Cfg::FN / 2, true>(cur, a_off, b_off, s_off, sb, af, cs, acc);
+            if (lag)
+                sync_and_load(c + 1);
+            compute_part<Cfg, SI, Cfg::FN / 2, Cfg::FN, false>(cur, a_off, b_off, s_off, sb, af, cs,
+                                                               acc);
+            slot = slot == 2 ? 0 : slot + 1;
+        }
+        if (!lag && KB > 0)
+            sync_and_load(KB);
+    } else {
     // prologue: the first STAGES-1 chunks in flight
 #pragma unroll
     for (int st = 0; st < Cfg::STAGES - 1; ++st)
         if (st < KB)
             load_stage<Cfg, SI>(smem + st * Cfg::STAGE, A, sA, B, M, N, K, m0, n0, st, wave, lane);
 
-    // scale_B of the wave's column block, loaded one chunk ahead: the scalar load then
-    // completes under the LDS barrier's wait instead of stalling the chunk's LDS reads
-    const typename SI::T* const sB_col = sB + (nb_wave < NB ? nb_wave : NB - 1);
-    float sb_next = KB > 0 ? SI::value(sB_col[0]) : 0.0f;
     for (int64_t kb = 0; kb < KB; ++kb) {
         const uint8_t LDS* cur = smem + (kb % Cfg::STAGES) * Cfg::STAGE;
         // chunk kb has landed once only the later chunks' loads may still be outstanding
@@ -380,14 +514,22 @@ __global__ __launch_bounds__(Cfg::NT) void gemm_fp8_blockscaled_kernel(
         lds_barrier();
         const float sb = sb_next;
         const int64_t nxt = kb + Cfg::STAGES - 1;
+#if FGQ_SPREAD_DMA
+        // chunk nxt's loads go out a few at a time between this chunk's column blocks
+        const StageLoader<Cfg, SI> loader{smem + (nxt % Cfg::STAGES) * Cfg::STAGE, A, sA, B, M, N,
+                                          K, m0, n0, nxt, wave, lane, nxt < KB};
+#else
         if (nxt < KB)
             load_stage<Cfg, SI>(smem + (nxt % Cfg::STAGES) * Cfg::STAGE, A, sA, B, M, N, K, m0, n0,
                             nxt, wave, lane);
+        const NoLoader loader;
+#endif
         if (kb + 1 < KB)
             sb_next = SI::value(sB_col[(kb + 1) * NB]);
-        compute_chunk<Cfg, SI>(cur, a_off, b_off, s_off, sb, acc);
+        compute_chunk<Cfg, SI>(cur, a_off, b_off, s_off, sb, acc, loader);
         if (Cfg::STAGES == 2)
             lds_barrier();   // chunk kb fully read before the next iteration refills it
+    }
     }
 
     static_assert(!FUSE || Cfg::BN >= 128, "the fused epilogue needs whole 128-column groups");
