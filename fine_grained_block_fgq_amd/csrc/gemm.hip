@@ -47,12 +47,9 @@
 
 namespace fgq {
 
-template <int BM_, int BN_, int WM_, int WN_, int STAGES_, bool PP_ = false>
+template <int BM_, int BN_, int WM_, int WN_, int STAGES_>
 struct GemmCfg {
     static constexpr int BM = BM_, BN = BN_, WM = WM_, WN = WN_, STAGES = STAGES_;
-    // PP: the second half of the waves (one per SIMD) runs half a chunk behind the first
-    // (see the wide kernel's main loop); needs a 3-stage ring
-    static constexpr bool PP = PP_;
     static constexpr int NW = WM * WN, NT = 64 * NW;
     static constexpr int TM = BM / WM, TN = BN / WN;
     static constexpr int FM = TM / 16, FN = TN / 16;
@@ -68,7 +65,6 @@ struct GemmCfg {
     static_assert(A_LOADS % NW == 0 && B_LOADS % NW == 0, "loads split evenly over waves");
     static_assert(S_LOADS <= NW, "one scale load per wave at most");
     static_assert(STAGES >= 2 && STAGES <= 4, "LDS ring depth");
-    static_assert(!PP || (STAGES == 3 && NW == 8 && FN % 2 == 0), "ping-pong: 3 stages, 8 waves");
     static_assert(STAGES * STAGE <= 160 * 1024, "LDS capacity (160 KB per CU)");
     // 16-byte column swizzles.  gfx950 LDS has 64 banks of 4 bytes (256 B per cycle): a
     // ds_read_b128 serves 16 lanes per cycle, a ds_read_b64(_tr) 32 lanes.  A rows are 128 B
@@ -181,17 +177,9 @@ __device__ __forceinline__ void load_stage(uint8_t LDS* stage, const uint8_t* __
 // blocks of the previous chunk's compute: issued all at once right after a barrier, the 56
 // loads of the eight waves queue at the CU's address unit (about 1 KB per 16 cycles) and
 // hold every wave for hundreds of cycles while its SIMD's matrix core idles.
-#ifndef FGQ_DMA_WAVES
-#define FGQ_DMA_WAVES 0
-#endif
 template <class Cfg, class SI>
 struct StageLoader {
-    // loading waves: all, or (FGQ_DMA_WAVES) only the first ones -- one per SIMD, the waves
-    // that the SIMD's arbiter favours, so that the issue stalls fall on them
-    static constexpr int LW = (FGQ_DMA_WAVES > 0 && FGQ_DMA_WAVES < Cfg::NW) ? FGQ_DMA_WAVES : Cfg::NW;
-    static_assert(Cfg::A_LOADS % LW == 0 && Cfg::B_LOADS % LW == 0 && Cfg::S_LOADS <= LW,
-                  "loads split evenly over the loading waves");
-    static constexpr int NA = Cfg::A_LOADS / LW, NBL = Cfg::B_LOADS / LW;
+    static constexpr int NA = Cfg::A_LOADS / Cfg::NW, NBL = Cfg::B_LOADS / Cfg::NW;
     static constexpr int PIECES = NA + NBL + 1;
     // pieces per column block, over the first FN-1 blocks (the last block issues none, so
     // the last piece still has most of a chunk to land)
@@ -207,14 +195,14 @@ struct StageLoader {
     __device__ __forceinline__ void piece(int pc) const
     {
         if (pc < NA) {
-            const int ia = pc * LW + wave;
+            const int ia = pc * Cfg::NW + wave;
             const int row = ia * 8 + (lane >> 3);
             const int c = (lane & 7) ^ Cfg::a_swz(row);
             int64_t gm = m0 + row;
             gm = gm < M ? gm : M - 1;
             dma_b128(A + gm * K + kb * 128 + c * 16, lds_addr(stage + ia * 1024));
         } else if (pc < NA + NBL) {
-            const int ib = (pc - NA) * LW + wave;
+            const int ib = (pc - NA) * Cfg::NW + wave;
             const int k = ib * Cfg::B_ROWS_PER_LOAD + lane / Cfg::B_CHUNKS;
             const int q = lane % Cfg::B_CHUNKS;
             const int c = q ^ Cfg::b_swz(k);
@@ -231,7 +219,7 @@ struct StageLoader {
     // the pieces that go out just before column block j
     __device__ __forceinline__ void before_block(int j) const
     {
-        if (!active || wave >= LW)
+        if (!active)
             return;
 #pragma unroll
         for (int pc = j * PER; pc < (j + 1) * PER && pc < PIECES; ++pc)
@@ -453,46 +441,6 @@ __global__ __launch_bounds__(Cfg::NT) void gemm_fp8_blockscaled_kernel(
     const typename SI::T* const sB_col = sB + (nb_wave < NB ? nb_wave : NB - 1);
     float sb_next = KB > 0 ? SI::value(sB_col[0]) : 0.0f;
 
-    if constexpr (Cfg::PP) {
-        // Ping-pong schedule.  Every wave computes chunk after chunk, each chunk as a first
-        // half (scales, A operands, column blocks 0..FN/2-1) then a second half; barrier k
-        // (chunk k landed everywhere; chunk k+1's loads then go out) comes before chunk k's
-        // first half in the leading waves (0..3, one per SIMD) and before chunk k-1's second
-        // half in the lagging waves (4..7).  So on every SIMD one wave is in the MFMA-heavy
-        // middle of a chunk while the other reads and converts the start of one.  Between
-        // barriers k and k+1 chunks k-1 and k are read, so slot (k+1) % 3, last read before
-        // barrier k, takes chunk k+1.
-        const bool lag = wave >= Cfg::NW / 2;
-        int slot = 0;   // ring slot of chunk c
-        auto sync_and_load = [&](int64_t k) {   // barrier k
-            wait_vm<0>();    // this wave's loads of chunk k have landed
-            lds_barrier();   // ... everyone's
-            if (k + 1 < KB)
-                load_stage<Cfg, SI>(smem + ((k + 1) % 3) * Cfg::STAGE, A, sA, B, M, N, K, m0, n0,
-                                    k + 1, wave, lane);
-        };
-        if (KB > 0)
-            load_stage<Cfg, SI>(smem, A, sA, B, M, N, K, m0, n0, 0, wave, lane);
-        sync_and_load(0);
-        for (int64_t c = 0; c < KB; ++c) {
-            if (!lag && c > 0)
-                sync_and_load(c);
-            const float sb = sb_next;
-            if (c + 1 < KB)
-                sb_next = SI::value(sB_col[(c + 1) * NB]);
-            const uint8_t LDS* cur = smem + slot * Cfg::STAGE;
-            f16x8 af[Cfg::FM][4];
-            f32x4 cs[Cfg::FM];
-            compute_part<Cfg, SI, 0, Cfg::FN / 2, true>(cur, a_off, b_off, s_off, sb, af, cs, acc);
-            if (lag)
-                sync_and_load(c + 1);
-            compute_part<Cfg, SI, Cfg::FN / 2, Cfg::FN, false>(cur, a_off, b_off, s_off, sb, af, cs,
-                                                               acc);
-            slot = slot == 2 ? 0 : slot + 1;
-        }
-        if (!lag && KB > 0)
-            sync_and_load(KB);
-    } else {
     // prologue: the first STAGES-1 chunks in flight
 #pragma unroll
     for (int st = 0; st < Cfg::STAGES - 1; ++st)
@@ -528,8 +476,7 @@ __global__ __launch_bounds__(Cfg::NT) void gemm_fp8_blockscaled_kernel(
             sb_next = SI::value(sB_col[(kb + 1) * NB]);
         compute_chunk<Cfg, SI>(cur, a_off, b_off, s_off, sb, acc, loader);
         if (Cfg::STAGES == 2)
-            lds_barrier();   // chunk kb fully read before the next iteration refills it
-    }
+            lds_barrier();   // keeps the waves in step (measured faster than letting them drift)
     }
 
     static_assert(!FUSE || Cfg::BN >= 128, "the fused epilogue needs whole 128-column groups");
