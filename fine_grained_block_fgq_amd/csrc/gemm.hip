@@ -55,6 +55,9 @@ struct GemmCfg {
     static constexpr int FM = TM / 16, FN = TN / 16;
     static constexpr int A_BYTES = BM * 128, B_BYTES = 128 * BN, S_BYTES = BM * 4;
     static constexpr int STAGE = A_BYTES + B_BYTES + S_BYTES;
+    // the bf16 tile staged for the epilogue: rows of BN values plus 16 bytes
+    static constexpr int STAGED_LD = BN * 2 + 16;
+    static constexpr int SMEM = STAGES * STAGE > BM * STAGED_LD ? STAGES * STAGE : BM * STAGED_LD;
     static constexpr int A_LOADS = A_BYTES / 1024;   // 1 KB per wave instruction
     static constexpr int B_LOADS = B_BYTES / 1024;
     static constexpr int S_LOADS = BM / 64;           // 256 B per wave instruction
@@ -65,7 +68,7 @@ struct GemmCfg {
     static_assert(A_LOADS % NW == 0 && B_LOADS % NW == 0, "loads split evenly over waves");
     static_assert(S_LOADS <= NW, "one scale load per wave at most");
     static_assert(STAGES >= 2 && STAGES <= 4, "LDS ring depth");
-    static_assert(STAGES * STAGE <= 160 * 1024, "LDS capacity (160 KB per CU)");
+    static_assert(SMEM <= 160 * 1024, "LDS capacity (160 KB per CU)");
     // 16-byte column swizzles.  gfx950 LDS has 64 banks of 4 bytes (256 B per cycle): a
     // ds_read_b128 serves 16 lanes per cycle, a ds_read_b64(_tr) 32 lanes.  A rows are 128 B
     // (two per bank line): the 16 rows of a fragment read in one cycle take 16 distinct
@@ -172,6 +175,32 @@ __device__ __forceinline__ void load_stage(uint8_t LDS* stage, const uint8_t* __
     }
 }
 
+// LDS byte offsets of a wave's operand fragments inside a stage.  A: fragment i (rows
+// row0 + 16i + q) is a0/a1 + 2048*i -- the row swizzle (row/2)%8 does not change with i -- so
+// the 16 offsets are two registers plus immediates.  B: the wave's column block j is 16-byte
+// chunk ch0 + j; with ch0 a multiple of the power-of-two FN, (ch0 + j) ^ swz = (ch0 ^ swz) ^ j
+// and the address fields (k*BN, chunk*16, half*8) occupy disjoint bits, so block j's offset
+// for sub-step t is b[t] ^ 16*j.
+template <class Cfg>
+struct FragOffsets {
+    static_assert((Cfg::FN & (Cfg::FN - 1)) == 0, "power-of-two column blocks per wave");
+    int a0, a1;
+    int b[4];
+    __device__ __forceinline__ FragOffsets(int row0, int ch0, int g, int q)
+    {
+        const int row = row0 + q;
+        a0 = row * 128 + (((2 * g) ^ Cfg::a_swz(row)) * 16);
+        a1 = row * 128 + (((2 * g + 1) ^ Cfg::a_swz(row)) * 16);
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+            const int k = 32 * g + 8 * t + (q >> 1);
+            b[t] = Cfg::A_BYTES + k * Cfg::BN + ((ch0 ^ Cfg::b_swz(k)) * 16) + 8 * (q & 1);
+        }
+    }
+    __device__ __forceinline__ int a(int i, int h) const { return (h ? a1 : a0) + 2048 * i; }
+    __device__ __forceinline__ int bo(int j, int t) const { return b[t] ^ (16 * j); }
+};
+
 // The wave's direct-to-LDS loads of one stage as separately issued pieces (A loads, then B
 // loads, then the scale load), so that a chunk's refill can be spread over the column
 // blocks of the previous chunk's compute: issued all at once right after a barrier, the 56
@@ -237,8 +266,8 @@ struct NoLoader {
 // in registers for the chunk's later parts).  Per tile: f16 operands, four chained f16
 // MFMAs, then acc += P * (sA*sB).
 template <class Cfg, class SI, int J0, int J1, bool FIRST, class Loader = NoLoader>
-__device__ __forceinline__ void compute_part(const uint8_t LDS* cur, const int (&a_off)[Cfg::FM][2],
-                                             const int (&b_off)[Cfg::FN][4], int s_off, float sb,
+__device__ __forceinline__ void compute_part(const uint8_t LDS* cur, const FragOffsets<Cfg>& fo,
+                                             int s_off, float sb,
                                              f16x8 (&af)[Cfg::FM][4], f32x4 (&cs)[Cfg::FM],
                                              f32x4 (&acc)[Cfg::FM][Cfg::FN],
                                              const Loader& loader = Loader())
@@ -252,15 +281,15 @@ __device__ __forceinline__ void compute_part(const uint8_t LDS* cur, const int (
         // A operands: lane bytes 8t..8t+7 of its 32 (k = 32g + 8t + b) -> sub-step t
 #pragma unroll
         for (int i = 0; i < Cfg::FM; ++i) {
-            araw[i][0] = *(const i32x4 LDS*)(cur + a_off[i][0]);
-            araw[i][1] = *(const i32x4 LDS*)(cur + a_off[i][1]);
+            araw[i][0] = *(const i32x4 LDS*)(cur + fo.a(i, 0));
+            araw[i][1] = *(const i32x4 LDS*)(cur + fo.a(i, 1));
         }
     }
     // B operands: transposed read t gives k = 32g + 8t + b for column q -> sub-step t
     i32x2 braw[2][4];
 #pragma unroll
     for (int t = 0; t < 4; ++t)
-        braw[0][t] = __builtin_amdgcn_ds_read_tr8_b64_v2i32((i32x2 LDS*)(cur + b_off[J0][t]));
+        braw[0][t] = __builtin_amdgcn_ds_read_tr8_b64_v2i32((i32x2 LDS*)(cur + fo.bo(J0, t)));
     if constexpr (FIRST) {
 #pragma unroll
         for (int i = 0; i < Cfg::FM; ++i) {
@@ -277,7 +306,7 @@ __device__ __forceinline__ void compute_part(const uint8_t LDS* cur, const int (
 #pragma unroll
             for (int t = 0; t < 4; ++t)
                 braw[(j + 1 - J0) & 1][t] =
-                    __builtin_amdgcn_ds_read_tr8_b64_v2i32((i32x2 LDS*)(cur + b_off[j + 1][t]));
+                    __builtin_amdgcn_ds_read_tr8_b64_v2i32((i32x2 LDS*)(cur + fo.bo(j + 1, t)));
         }
         f16x8 bf[4];
 #pragma unroll
@@ -303,14 +332,14 @@ __device__ __forceinline__ void compute_part(const uint8_t LDS* cur, const int (
 
 // One whole 128-K chunk (and, with a StageLoader, the refill of another stage).
 template <class Cfg, class SI, class Loader = NoLoader>
-__device__ __forceinline__ void compute_chunk(const uint8_t LDS* cur, const int (&a_off)[Cfg::FM][2],
-                                              const int (&b_off)[Cfg::FN][4], int s_off, float sb,
+__device__ __forceinline__ void compute_chunk(const uint8_t LDS* cur, const FragOffsets<Cfg>& fo,
+                                              int s_off, float sb,
                                               f32x4 (&acc)[Cfg::FM][Cfg::FN],
                                               const Loader& loader = Loader())
 {
     f16x8 af[Cfg::FM][4];
     f32x4 cs[Cfg::FM];
-    compute_part<Cfg, SI, 0, Cfg::FN, true>(cur, a_off, b_off, s_off, sb, af, cs, acc, loader);
+    compute_part<Cfg, SI, 0, Cfg::FN, true>(cur, fo, s_off, sb, af, cs, acc, loader);
 #if FGQ_SCHED == 1
     __builtin_amdgcn_iglp_opt(0);
 #elif FGQ_SCHED == 2
@@ -334,8 +363,7 @@ __device__ __forceinline__ void store_quant_tile(uint8_t LDS* smem,
 {
     // staged row: BN bf16 plus 16 bytes, so the four row groups 4g+r written together by a
     // wave land on different banks
-    constexpr int LD = Cfg::BN * 2 + 16;
-    static_assert(Cfg::BM * LD <= Cfg::STAGES * Cfg::STAGE, "staged tile fits the LDS ring");
+    constexpr int LD = Cfg::STAGED_LD;
 #pragma unroll
     for (int i = 0; i < Cfg::FM; ++i)
 #pragma unroll
@@ -378,7 +406,10 @@ __global__ __launch_bounds__(Cfg::NT) void gemm_fp8_blockscaled_kernel(
     void* __restrict__ Cout, int64_t M, int64_t N, int64_t K, int64_t n_begin, int64_t n_end,
     uint8_t* __restrict__ Cq = nullptr, float* __restrict__ sC = nullptr)
 {
-    __shared__ __attribute__((aligned(1024))) uint8_t smem_raw[Cfg::STAGES * Cfg::STAGE];
+    // the ring, or the staged bf16 tile of the epilogue where that is larger
+    constexpr bool STAGED = FUSE || (OUT_BF16 && FGQ_STAGED_STORE && Cfg::BN >= 128);
+    __shared__ __attribute__((aligned(1024)))
+    uint8_t smem_raw[STAGED ? Cfg::SMEM : Cfg::STAGES * Cfg::STAGE];
     uint8_t LDS* const smem = (uint8_t LDS*)smem_raw;
 
     const int lane = threadIdx.x & 63;
@@ -409,23 +440,7 @@ __global__ __launch_bounds__(Cfg::NT) void gemm_fp8_blockscaled_kernel(
     const int q = lane & 15;      // row (A) / column (B) within a 16x16 fragment
 
     // per-lane LDS offsets inside a stage
-    int a_off[Cfg::FM][2];
-#pragma unroll
-    for (int i = 0; i < Cfg::FM; ++i) {
-        const int row = wm * Cfg::TM + 16 * i + q;
-        a_off[i][0] = row * 128 + (((2 * g) ^ Cfg::a_swz(row)) * 16);
-        a_off[i][1] = row * 128 + (((2 * g + 1) ^ Cfg::a_swz(row)) * 16);
-    }
-    int b_off[Cfg::FN][4];
-#pragma unroll
-    for (int j = 0; j < Cfg::FN; ++j) {
-        const int ch = (wn * Cfg::TN + 16 * j) / 16;
-#pragma unroll
-        for (int t = 0; t < 4; ++t) {
-            const int k = 32 * g + 8 * t + (q >> 1);
-            b_off[j][t] = Cfg::A_BYTES + k * Cfg::BN + ((ch ^ Cfg::b_swz(k)) * 16) + 8 * (q & 1);
-        }
-    }
+    const FragOffsets<Cfg> fo(wm * Cfg::TM, wn * Cfg::FN, g, q);
     const int s_off = Cfg::A_BYTES + Cfg::B_BYTES + (wm * Cfg::TM + 4 * g) * 4;
     const int64_t nb_wave = (n0 + wn * Cfg::TN) / 128;
 
@@ -474,13 +489,13 @@ __global__ __launch_bounds__(Cfg::NT) void gemm_fp8_blockscaled_kernel(
 #endif
         if (kb + 1 < KB)
             sb_next = SI::value(sB_col[(kb + 1) * NB]);
-        compute_chunk<Cfg, SI>(cur, a_off, b_off, s_off, sb, acc, loader);
+        compute_chunk<Cfg, SI>(cur, fo, s_off, sb, acc, loader);
         if (Cfg::STAGES == 2)
             lds_barrier();   // keeps the waves in step (measured faster than letting them drift)
     }
 
     static_assert(!FUSE || Cfg::BN >= 128, "the fused epilogue needs whole 128-column groups");
-    if constexpr (FUSE || (OUT_BF16 && FGQ_STAGED_STORE && Cfg::BN >= 128)) {
+    if constexpr (STAGED) {
         // bf16 C leaves through an LDS-staged tile: 16-byte row-contiguous stores (and, fused,
         // the quantization of every row group)
         lds_barrier();   // every wave is done with the ring: it becomes the staging tile
@@ -569,23 +584,7 @@ __global__ __launch_bounds__(Cfg::NT * KG) void gemm_fp8_blockscaled_ksplit_kern
     const int64_t KB = K / 128, NB = N / 128;
     const int64_t steps = (KB + KG - 1) / KG;
 
-    int a_off[Cfg::FM][2];
-#pragma unroll
-    for (int i = 0; i < Cfg::FM; ++i) {
-        const int row = wm * Cfg::TM + 16 * i + q;
-        a_off[i][0] = row * 128 + (((2 * g) ^ Cfg::a_swz(row)) * 16);
-        a_off[i][1] = row * 128 + (((2 * g + 1) ^ Cfg::a_swz(row)) * 16);
-    }
-    int b_off[Cfg::FN][4];
-#pragma unroll
-    for (int j = 0; j < Cfg::FN; ++j) {
-        const int ch = (wn * Cfg::TN + 16 * j) / 16;
-#pragma unroll
-        for (int t = 0; t < 4; ++t) {
-            const int k = 32 * g + 8 * t + (q >> 1);
-            b_off[j][t] = Cfg::A_BYTES + k * Cfg::BN + ((ch ^ Cfg::b_swz(k)) * 16) + 8 * (q & 1);
-        }
-    }
+    const FragOffsets<Cfg> fo(wm * Cfg::TM, wn * Cfg::FN, g, q);
     const int s_off = Cfg::A_BYTES + Cfg::B_BYTES + (wm * Cfg::TM + 4 * g) * 4;
     const int64_t nb = (n0 + wn * Cfg::TN) / 128;
 
@@ -623,7 +622,7 @@ __global__ __launch_bounds__(Cfg::NT * KG) void gemm_fp8_blockscaled_ksplit_kern
                                 lane);
         if (kb < KB) {
             const float sb = SI::value(sB[kb * NB + nb]);
-            compute_chunk<Cfg, SI>(stage_of(st), a_off, b_off, s_off, sb, acc);
+            compute_chunk<Cfg, SI>(stage_of(st), fo, s_off, sb, acc);
         }
         if (Cfg::STAGES == 2)
             lds_barrier();
@@ -708,6 +707,9 @@ struct NarrowCfg {
     static constexpr int FM = BM / 16, FN = 2;
     static constexpr int A_BYTES = BM * 128, B_BYTES = 128 * BN, S_BYTES = 256;
     static constexpr int STAGE = A_BYTES + B_BYTES + S_BYTES;
+    // the bf16 tile staged for the epilogue: rows of BN values plus 16 bytes
+    static constexpr int STAGED_LD = BN * 2 + 16;
+    static constexpr int SMEM = STAGES * STAGE > BM * STAGED_LD ? STAGES * STAGE : BM * STAGED_LD;
     static constexpr int A_LOADS = A_BYTES / 1024, B_LOADS = B_BYTES / 1024;
     static constexpr int LOADS = A_LOADS + B_LOADS + 1;   // per chunk and wave
     static constexpr int RED_LD = BN + 4;                  // padded row of the reduction
@@ -779,21 +781,7 @@ __global__ __launch_bounds__(Cfg::NT) void gemm_fp8_blockscaled_narrow_kernel(
     const int64_t KB = K / 128, NB = N / 128, nb = n0 / 128;
 
     uint8_t LDS* const ring = smem + wave * (Cfg::STAGES * Cfg::STAGE);
-    int a_off[Cfg::FM][2];
-#pragma unroll
-    for (int i = 0; i < Cfg::FM; ++i) {
-        const int row = 16 * i + q;
-        a_off[i][0] = row * 128 + (((2 * g) ^ Cfg::a_swz(row)) * 16);
-        a_off[i][1] = row * 128 + (((2 * g + 1) ^ Cfg::a_swz(row)) * 16);
-    }
-    int b_off[Cfg::FN][4];
-#pragma unroll
-    for (int j = 0; j < Cfg::FN; ++j)
-#pragma unroll
-        for (int t = 0; t < 4; ++t) {
-            const int k = 32 * g + 8 * t + (q >> 1);
-            b_off[j][t] = Cfg::A_BYTES + k * Cfg::BN + ((j ^ Cfg::b_swz(k)) * 16) + 8 * (q & 1);
-        }
+    const FragOffsets<Cfg> fo(0, 0, g, q);
     const int s_off = Cfg::A_BYTES + Cfg::B_BYTES + 4 * g * 4;
 
     f32x4 acc[Cfg::FM][Cfg::FN];
@@ -825,7 +813,7 @@ __global__ __launch_bounds__(Cfg::NT) void gemm_fp8_blockscaled_narrow_kernel(
                              n0, wave + nxt * Cfg::KW, lane);
         const int64_t kb = wave + c * Cfg::KW;
         const float sb = SI::value(sB[kb * NB + nb]);
-        compute_chunk<Cfg, SI>(ring + (c % Cfg::STAGES) * Cfg::STAGE, a_off, b_off, s_off, sb, acc);
+        compute_chunk<Cfg, SI>(ring + (c % Cfg::STAGES) * Cfg::STAGE, fo, s_off, sb, acc);
     }
 
     // sum the KW partial tiles in wave order, then store coalesced
