@@ -147,7 +147,7 @@ def summarize(ktrace_dir, fetch_dir, write_dir):
                                                      "bytes_per_launch": b}
     with open(os.path.join(PROFILES, "kernel_stats_bench_step.txt"), "w") as f:
         f.write("command: cd /tmp && export TMPDIR=/tmp; rocprofv3 --kernel-trace --stats -f csv "
-                "-d <dir> -o run -- python3 bench.py --steps 20 --warmup 5 --no-cpu-baseline\n"
+                "-d <dir> -o run -- python3 bench.py --no-cpu-baseline\n"
                 "summary: python3 bench.py --summarize <ktrace dir> <fetch dir> <write dir>\n\n")
         f.write(stats + "\n")
     with open(os.path.join(PROFILES, "hbm_traffic_counters.txt"), "w") as f:
@@ -227,8 +227,10 @@ def profile_pass(torch, fgq, synth, dev, reps=3):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=10)
+    # the GPU reaches its steady clock after ~30 ms of this work (a cold start runs the
+    # first steps ~25% slower), so the default warmup is 300 steps (~50 ms)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=300)
     ap.add_argument("--quant-reps", type=int, default=50)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--summarize", nargs=3, metavar=("KTRACE_DIR", "FETCH_DIR", "WRITE_DIR"),
@@ -276,23 +278,20 @@ def main():
     stream = torch.cuda.current_stream()
 
     def step(ev=None):
-        if ev is not None:
-            ev[0].record(stream)
         fgq.fgq_quantize_act_1x128(A, Aq, sA, stream)
-        if ev is not None:
-            ev[1].record(stream)
         fgq.fgq_quantize_weight_128x128(B, Bq, sB, stream)
         if ev is not None:
-            ev[2].record(stream)
+            ev[0].record(stream)
         fgq.fgq_gemm_fp8_blockscaled(Aq, sA, Bq, sB, C, stream=stream)
         if ev is not None:
-            ev[3].record(stream)
+            ev[1].record(stream)
 
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
-    # timed region: exactly `steps` steps; HIP events on the launch stream bracket each kernel
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    # timed region: exactly `steps` steps; HIP events on the launch stream bracket each GEMM
+    # (the dominant kernel; events between every kernel would add their own gaps)
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for e in evs:
@@ -300,9 +299,18 @@ def main():
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     ms_per_step = (t1 - t0) * 1e3 / args.steps
-    qa_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in evs]))
-    qw_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in evs]))
-    gm_ms = float(np.mean([e[2].elapsed_time(e[3]) for e in evs]))
+    gm_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in evs]))
+    # the two quantizers of the step, each between its own events (outside the timed steps)
+    qev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(50)]
+    for e in qev:
+        e[0].record(stream)
+        fgq.fgq_quantize_act_1x128(A, Aq, sA, stream)
+        e[1].record(stream)
+        fgq.fgq_quantize_weight_128x128(B, Bq, sB, stream)
+        e[2].record(stream)
+    torch.cuda.synchronize()
+    qa_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in qev]))
+    qw_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in qev]))
     flops = 2.0 * M * N * K
     gemm_tflops = flops / (gm_ms * 1e-3) / 1e12
     log(f"step {ms_per_step:.4f} ms | quant A {qa_ms*1e3:.1f} us  quant B {qw_ms*1e3:.1f} us  "
@@ -393,7 +401,8 @@ def main():
     Xs = [to_dev_bf16(X_bits, torch) for _ in range(nbuf)]
     Xqs = [torch.empty((Mq, Kq), dtype=torch.uint8, device=dev) for _ in range(nbuf)]
     sXs = [torch.empty((Mq, Kq // 128), dtype=torch.float32, device=dev) for _ in range(nbuf)]
-    for i in range(nbuf):
+    for r in range(8 * nbuf):   # warm again after the host-side input generation
+        i = r % nbuf
         fgq.fgq_quantize_act_1x128(Xs[i], Xqs[i], sXs[i], stream)
     torch.cuda.synchronize()
     qev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
