@@ -68,10 +68,12 @@ def profiled_traffic(key, kind):
     return rec["bytes_per_launch"]
 
 
-def summarize(ktrace_dir, fetch_dir, write_dir):
+def summarize(ktrace_dir, fetch_dir, write_dir, mfma_dir=None):
     """Write the profile summaries under profiles/ from rocprofv3 csv output directories:
     a --kernel-trace --stats run of bench.py, and --pmc FETCH_SIZE / --pmc WRITE_SIZE runs of
-    `bench.py --mode profile` (which includes a 512 MiB copy used to calibrate both counters)."""
+    `bench.py --mode profile` (which includes a 512 MiB copy used to calibrate both counters),
+    and optionally a --pmc SQ_INSTS_MFMA run of the same (MFMA instruction count per GEMM
+    against 2*M*N*K / 16384 flop per 16x16x32 instruction)."""
     import csv
     import glob
 
@@ -157,6 +159,20 @@ def summarize(ktrace_dir, fetch_dir, write_dir):
         f.write("\n".join(out) + "\n")
     with open(os.path.join(PROFILES, "traffic.json"), "w") as f:
         json.dump(traffic, f, indent=1)
+    if mfma_dir:
+        mf = counter(mfma_dir, "SQ_INSTS_MFMA")
+        mlines = ["rocprofv3 --pmc SQ_INSTS_MFMA per dispatch (median over dispatches); a 16x16x32 "
+                  "f16 MFMA is 16384 flop, so the GEMM's count x 16384 should equal 2*M*N*K",
+                  f"{'kernel':40s} {'grid':>9s} {'SQ_INSTS_MFMA':>14s} {'x16384 flop':>14s}"]
+        for k in sorted(mf):
+            v = sorted(mf[k])[len(mf[k]) // 2]
+            mlines.append(f"{k[0]:40s} {k[1]:9d} {v:14.0f} {v * 16384:14.4g}")
+        mlines.append(f"2*4096^3 = {2 * 4096**3:.4g} flop")
+        with open(os.path.join(PROFILES, "mfma_count_counters.txt"), "w") as f:
+            f.write("command: rocprofv3 --pmc SQ_INSTS_MFMA -f csv -d <dir> -o run -- python3 "
+                    "bench.py --mode profile\n\n")
+            f.write("\n".join(mlines) + "\n")
+        print("\n".join(mlines))
     print(stats)
     print("\n".join(out))
 
@@ -233,7 +249,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=300)
     ap.add_argument("--quant-reps", type=int, default=50)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--summarize", nargs=3, metavar=("KTRACE_DIR", "FETCH_DIR", "WRITE_DIR"),
+    ap.add_argument("--summarize", nargs="+", metavar="DIR",
                     help="write profiles/ summaries from rocprofv3 csv output and exit")
     ap.add_argument("--mode", choices=["bench", "profile"], default="bench",
                     help="profile: a short pass for hardware-counter runs -- the GEMM, both "
@@ -311,8 +327,25 @@ def main():
     torch.cuda.synchronize()
     qa_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in qev]))
     qw_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in qev]))
+    gm_all = np.array([e[0].elapsed_time(e[1]) for e in evs])
     flops = 2.0 * M * N * K
     gemm_tflops = flops / (gm_ms * 1e-3) / 1e12
+    # measured ceiling: f16 MFMAs only (the partials' instruction), two waves per SIMD on
+    # every CU, ~1 ms per launch, at the same (warm) clock
+    ncu = torch.cuda.get_device_properties(dev).multi_processor_count
+    cal_out = torch.empty((2 * ncu * 512,), dtype=torch.float32, device=dev)
+    cal_iters = 2000
+    fgq.fgq_calib_mfma_f16(cal_out, 2 * ncu, cal_iters, stream)
+    cev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(10)]
+    for a, b in cev:
+        a.record(stream)
+        cal_flops = fgq.fgq_calib_mfma_f16(cal_out, 2 * ncu, cal_iters, stream)
+        b.record(stream)
+    torch.cuda.synchronize()
+    mfma_ceiling = cal_flops / (float(np.median([a.elapsed_time(b) for a, b in cev])) * 1e-3) / 1e12
+    del cal_out
+    log(f"MFMA-only ceiling (16x16x32 f16): {mfma_ceiling:.0f} TFLOP/s")
     log(f"step {ms_per_step:.4f} ms | quant A {qa_ms*1e3:.1f} us  quant B {qw_ms*1e3:.1f} us  "
         f"GEMM {gm_ms*1e3:.1f} us = {gemm_tflops:.0f} TFLOP/s")
 
@@ -424,6 +457,23 @@ def main():
     e1.record(stream)
     torch.cuda.synchronize()
     qb_ms = e0.elapsed_time(e1) / (4 * nbuf)
+    # measured ceiling: a streaming kernel with the same traffic (16 bytes read, 8 written per
+    # lane) over the same rotating buffers, per launch and back to back
+    sev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(args.quant_reps)]
+    for r, (a, b) in enumerate(sev):
+        i = r % nbuf
+        a.record(stream)
+        s_bytes = fgq.fgq_calib_stream(Xs[i], Xqs[i], stream)
+        b.record(stream)
+    e0.record(stream)
+    for r in range(4 * nbuf):
+        fgq.fgq_calib_stream(Xs[r % nbuf], Xqs[r % nbuf], stream)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    s_gbs = s_bytes / (float(np.mean([a.elapsed_time(b) for a, b in sev])) * 1e-3) / 1e9
+    sb_gbs = s_bytes / (e0.elapsed_time(e1) / (4 * nbuf) * 1e-3) / 1e9
+    log(f"same-traffic stream: {s_gbs:.0f} GB/s per launch, {sb_gbs:.0f} GB/s back to back")
     q_bytes = quant_act_bytes(Mq, Kq)
     q_gbs = q_bytes / (q_ms * 1e-3) / 1e9
     qb_gbs = q_bytes / (qb_ms * 1e-3) / 1e9
@@ -458,6 +508,10 @@ def main():
             "algorithmic_bytes": int(M * K + K * N + 4 * M * (K // 128)
                                      + 4 * (K // 128) * (N // 128) + 2 * M * N),
             "frac_f16_peak": round(gemm_tflops / PEAK_F16_TFLOPS, 4),
+            "median_us": round(float(np.median(gm_all)) * 1e3, 2),
+            "min_us": round(float(gm_all.min()) * 1e3, 2),
+            "mfma_only_ceiling": round(mfma_ceiling, 1),
+            "frac_of_mfma_only_ceiling": round(gemm_tflops / mfma_ceiling, 4),
             "note": "partials use f16 MFMAs on exactly converted E4M3 operands (gfx950 FP8 "
                     "MFMA accumulation is too coarse for the fp32 tolerance); frac_f16_peak "
                     "is against the 2500 TFLOP/s dense f16 peak of that instruction",
@@ -475,6 +529,9 @@ def main():
             "us": round(q_ms * 1e3, 2),
             "back_to_back_GBps": round(qb_gbs, 1),
             "back_to_back_frac": round(qb_gbs / PEAK_HBM_GBS, 4),
+            "stream_ceiling_GBps": round(s_gbs, 1),
+            "frac_of_stream_ceiling": round(q_gbs / s_gbs, 4),
+            "back_to_back_frac_of_stream_ceiling": round(qb_gbs / sb_gbs, 4),
             "algorithmic_bytes": q_bytes,
             "traffic": profiled_traffic("quant_act_1x128 16384x7168", "quant_act"),
         },

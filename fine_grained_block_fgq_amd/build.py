@@ -7,7 +7,7 @@ import subprocess
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libfgq.so")
-SOURCES = ["quant.hip", "gemm.hip", "nvfp4.hip", "api.cpp"]
+SOURCES = ["quant.hip", "gemm.hip", "nvfp4.hip", "calib.hip", "api.cpp"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 FLAGS = [

@@ -269,4 +269,31 @@ int fgq_gemm_nvfp4(const void* A_q, const uint8_t* scale_A, const float* global_
                                                 static_cast<hipStream_t>(stream)));
 }
 
+int fgq_calib_stream(const void* src, void* dst, int64_t n16, void* stream)
+{
+    if (n16 < 0 || n16 > (int64_t(1) << 34))
+        return FGQ_ERR_SHAPE;
+    if (n16 == 0)
+        return FGQ_OK;
+    if (!src || !dst)
+        return FGQ_ERR_NULL;
+    if (misaligned(src) || misaligned(dst))
+        return FGQ_ERR_ALIGN;
+    if (overlap(src, 16 * n16, dst, 8 * n16))
+        return FGQ_ERR_ALIAS;
+    return launch_status(fgq::launch_calib_stream(src, dst, n16, static_cast<hipStream_t>(stream)));
+}
+
+int fgq_calib_mfma_f16(float* out, int64_t blocks, int64_t iters, void* stream)
+{
+    if (blocks < 1 || blocks > (int64_t(1) << 20) || iters < 0 || iters > (int64_t(1) << 24))
+        return FGQ_ERR_SHAPE;
+    if (!out)
+        return FGQ_ERR_NULL;
+    if (misaligned(out))
+        return FGQ_ERR_ALIGN;
+    return launch_status(
+        fgq::launch_calib_mfma_f16(out, blocks, iters, static_cast<hipStream_t>(stream)));
+}
+
 }  // extern "C"

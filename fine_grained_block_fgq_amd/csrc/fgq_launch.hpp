@@ -49,4 +49,10 @@ hipError_t launch_gemm_nvfp4(const void* A_q, const uint8_t* sA, const float* gA
                              const void* B_q, const uint8_t* sB, const float* gB, void* C,
                              int64_t M, int64_t N, int64_t K, int out_bf16, hipStream_t stream);
 
+// measured ceilings (calib.hip): a streaming kernel with the activation quantizer's traffic
+// (n16 lanes' worth: 16 bytes read from src and 8 written to dst each), and f16 MFMAs only
+// (blocks x 8 waves x iters x 16 MFMAs of 16x16x32; out holds blocks*512 floats)
+hipError_t launch_calib_stream(const void* src, void* dst, int64_t n16, hipStream_t stream);
+hipError_t launch_calib_mfma_f16(float* out, int64_t blocks, int64_t iters, hipStream_t stream);
+
 }  // namespace fgq

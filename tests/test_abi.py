@@ -152,3 +152,18 @@ G1, G2 = 0x80000, 0x90000
 ])
 def test_nvfp4_validation(fn, args, want):
     assert getattr(fgq.load(), fn)(*args, None) == want
+
+
+@pytest.mark.parametrize("fn,args,want", [
+    ("fgq_calib_stream", (P, Q, -1), -2),
+    ("fgq_calib_stream", (None, Q, 4), -1),
+    ("fgq_calib_stream", (P + 8, Q, 4), -3),
+    ("fgq_calib_stream", (P, P + 32, 4), -6),      # dst inside src
+    ("fgq_calib_stream", (None, None, 0), 0),     # empty: no-op
+    ("fgq_calib_mfma_f16", (P, 0, 10), -2),
+    ("fgq_calib_mfma_f16", (P, 4, -1), -2),
+    ("fgq_calib_mfma_f16", (None, 4, 10), -1),
+    ("fgq_calib_mfma_f16", (P + 4, 4, 10), -3),
+])
+def test_calib_validation(fn, args, want):
+    assert getattr(fgq.load(), fn)(*args, None) == want
