@@ -893,10 +893,10 @@ using CfgSmall = GemmCfg<FGQ_SMALL_CFG>;
 #endif
 using CfgNarrow = NarrowCfg<FGQ_NARROW_CFG>;
 #ifndef FGQ_SKINNY_CFG
-#define FGQ_SKINNY_CFG 128, 32, 4, 1, 3
+#define FGQ_SKINNY_CFG 128, 32, 4, 1, 2
 #endif
 #ifndef FGQ_SKINNY_KG
-#define FGQ_SKINNY_KG 2
+#define FGQ_SKINNY_KG 3
 #endif
 using CfgSkinny = GemmCfg<FGQ_SKINNY_CFG>;
 
