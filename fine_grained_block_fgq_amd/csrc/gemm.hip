@@ -553,7 +553,7 @@ static hipError_t launch_cfg(const void* A_q, const void* sA_, const void* B_q, 
 // Skinny shapes (M <= 128, decode-like): one workgroup per BM x 32 output tile with its K
 // chunks split over KG groups of NW waves.  Group c takes chunks c, c+KG, ...: a ring stage
 // holds KG chunks side by side, each loaded and computed by its own group with the wide
-// kernel's per-chunk code, so two waves share each SIMD (latency hiding) while the A/B
+// kernel's per-chunk code, so KG waves share each SIMD (latency hiding) while the A/B
 // stages stay within LDS.  The KG partial tiles are summed in LDS in group order (fixed:
 // results are repeatable bit for bit) and stored by group 0.
 template <class Cfg, class SI, bool OUT_BF16, int KG>
