@@ -261,57 +261,54 @@ struct NoLoader {
     __device__ __forceinline__ void before_block(int) const {}
 };
 
-// Part of one 128-K chunk of the wave's 16x16 tiles: the column blocks [J0, J1).  FIRST
-// parts also read the chunk's combined scales and convert the wave's A operands (both kept
-// in registers for the chunk's later parts).  Per tile: f16 operands, four chained f16
-// MFMAs, then acc += P * (sA*sB).
-template <class Cfg, class SI, int J0, int J1, bool FIRST, class Loader = NoLoader>
-__device__ __forceinline__ void compute_part(const uint8_t LDS* cur, const FragOffsets<Cfg>& fo,
-                                             int s_off, float sb,
-                                             f16x8 (&af)[Cfg::FM][4], f32x4 (&cs)[Cfg::FM],
-                                             f32x4 (&acc)[Cfg::FM][Cfg::FN],
-                                             const Loader& loader = Loader())
+// One 128-K chunk of the wave's 16x16 tiles (and, with a StageLoader, the refill of another
+// stage between its column blocks).  The chunk's combined scales and the wave's A operands
+// are read and converted once; then per column block j the B operands, four chained f16
+// MFMAs per tile, and acc += P * (sA*sB).
+template <class Cfg, class SI, class Loader = NoLoader>
+__device__ __forceinline__ void compute_chunk(const uint8_t LDS* cur, const FragOffsets<Cfg>& fo,
+                                              int s_off, float sb,
+                                              f32x4 (&acc)[Cfg::FM][Cfg::FN],
+                                              const Loader& loader = Loader())
 {
+    // combined scales for this lane's rows: sA[row, kb] * sB[kb, nb]
+    f32x4 cs[Cfg::FM];
+#pragma unroll
+    for (int i = 0; i < Cfg::FM; ++i)
+        cs[i] = SI::combine(cur + s_off + i * 64, sb);
+    // A operands: lane bytes 8t..8t+7 of its 32 (k = 32g + 8t + b) -> sub-step t
     i32x4 araw[Cfg::FM][2];
-    if constexpr (FIRST) {
-        // combined scales for this lane's rows: sA[row, kb] * sB[kb, nb]
 #pragma unroll
-        for (int i = 0; i < Cfg::FM; ++i)
-            cs[i] = SI::combine(cur + s_off + i * 64, sb);
-        // A operands: lane bytes 8t..8t+7 of its 32 (k = 32g + 8t + b) -> sub-step t
-#pragma unroll
-        for (int i = 0; i < Cfg::FM; ++i) {
-            araw[i][0] = *(const i32x4 LDS*)(cur + fo.a(i, 0));
-            araw[i][1] = *(const i32x4 LDS*)(cur + fo.a(i, 1));
-        }
+    for (int i = 0; i < Cfg::FM; ++i) {
+        araw[i][0] = *(const i32x4 LDS*)(cur + fo.a(i, 0));
+        araw[i][1] = *(const i32x4 LDS*)(cur + fo.a(i, 1));
     }
     // B operands: transposed read t gives k = 32g + 8t + b for column q -> sub-step t
     i32x2 braw[2][4];
 #pragma unroll
     for (int t = 0; t < 4; ++t)
-        braw[0][t] = __builtin_amdgcn_ds_read_tr8_b64_v2i32((i32x2 LDS*)(cur + fo.bo(J0, t)));
-    if constexpr (FIRST) {
+        braw[0][t] = __builtin_amdgcn_ds_read_tr8_b64_v2i32((i32x2 LDS*)(cur + fo.bo(0, t)));
+    f16x8 af[Cfg::FM][4];
 #pragma unroll
-        for (int i = 0; i < Cfg::FM; ++i) {
-            af[i][0] = e4m3x8_to_f16(araw[i][0][0], araw[i][0][1]);
-            af[i][1] = e4m3x8_to_f16(araw[i][0][2], araw[i][0][3]);
-            af[i][2] = e4m3x8_to_f16(araw[i][1][0], araw[i][1][1]);
-            af[i][3] = e4m3x8_to_f16(araw[i][1][2], araw[i][1][3]);
-        }
+    for (int i = 0; i < Cfg::FM; ++i) {
+        af[i][0] = e4m3x8_to_f16(araw[i][0][0], araw[i][0][1]);
+        af[i][1] = e4m3x8_to_f16(araw[i][0][2], araw[i][0][3]);
+        af[i][2] = e4m3x8_to_f16(araw[i][1][0], araw[i][1][1]);
+        af[i][3] = e4m3x8_to_f16(araw[i][1][2], araw[i][1][3]);
     }
 #pragma unroll
-    for (int j = J0; j < J1; ++j) {
+    for (int j = 0; j < Cfg::FN; ++j) {
         loader.before_block(j);
-        if (j + 1 < J1) {
+        if (j + 1 < Cfg::FN) {
 #pragma unroll
             for (int t = 0; t < 4; ++t)
-                braw[(j + 1 - J0) & 1][t] =
+                braw[(j + 1) & 1][t] =
                     __builtin_amdgcn_ds_read_tr8_b64_v2i32((i32x2 LDS*)(cur + fo.bo(j + 1, t)));
         }
         f16x8 bf[4];
 #pragma unroll
         for (int t = 0; t < 4; ++t)
-            bf[t] = e4m3x8_to_f16(braw[(j - J0) & 1][t][0], braw[(j - J0) & 1][t][1]);
+            bf[t] = e4m3x8_to_f16(braw[j & 1][t][0], braw[j & 1][t][1]);
         f32x4 p[Cfg::FM];
 #pragma unroll
         for (int i = 0; i < Cfg::FM; ++i)
@@ -328,18 +325,6 @@ __device__ __forceinline__ void compute_part(const uint8_t LDS* cur, const FragO
             for (int r = 0; r < 4; ++r)
                 acc[i][j][r] = __builtin_fmaf(p[i][r], cs[i][r], acc[i][j][r]);
     }
-}
-
-// One whole 128-K chunk (and, with a StageLoader, the refill of another stage).
-template <class Cfg, class SI, class Loader = NoLoader>
-__device__ __forceinline__ void compute_chunk(const uint8_t LDS* cur, const FragOffsets<Cfg>& fo,
-                                              int s_off, float sb,
-                                              f32x4 (&acc)[Cfg::FM][Cfg::FN],
-                                              const Loader& loader = Loader())
-{
-    f16x8 af[Cfg::FM][4];
-    f32x4 cs[Cfg::FM];
-    compute_part<Cfg, SI, 0, Cfg::FN, true>(cur, fo, s_off, sb, af, cs, acc, loader);
 #if FGQ_SCHED == 1
     __builtin_amdgcn_iglp_opt(0);
 #elif FGQ_SCHED == 2
