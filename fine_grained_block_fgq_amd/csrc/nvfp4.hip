@@ -27,8 +27,11 @@ __global__ void nvfp4_clear_kernel(uint32_t* slot)
 }
 
 // grid-stride max with four loads in flight per lane, reduced over the workgroup in LDS:
-// one atomic per workgroup (at most NVFP4_AMAX_BLOCKS of them on the one address)
-constexpr int NVFP4_AMAX_BLOCKS = 512;
+// one atomic per workgroup.  The atomics on the one address are serialized (~10 ns each,
+// measured: 4096 workgroups cost 40 us more than 512), so the grid is capped at 256
+// workgroups, each lane taking at least 16 vectors.
+constexpr int NVFP4_AMAX_BLOCKS = 256;
+constexpr int NVFP4_AMAX_VPT = 16;
 
 __global__ __launch_bounds__(256) void nvfp4_amax_kernel(const u32x4* __restrict__ X,
                                                          int64_t nvec, uint32_t* slot)
@@ -116,7 +119,7 @@ hipError_t launch_quant_nvfp4(const void* X, void* Xq, uint8_t* sX, float* g, in
     uint32_t* slot = reinterpret_cast<uint32_t*>(g);
     const int64_t nvec = R * C / 8;
     hipLaunchKernelGGL(nvfp4_clear_kernel, dim3(1), dim3(64), 0, stream, slot);
-    int64_t ablocks = (nvec + 256 * 16 - 1) / (256 * 16);
+    int64_t ablocks = (nvec + 256 * NVFP4_AMAX_VPT - 1) / (256 * NVFP4_AMAX_VPT);
     ablocks = ablocks < 1 ? 1 : (ablocks > NVFP4_AMAX_BLOCKS ? NVFP4_AMAX_BLOCKS : ablocks);
     hipLaunchKernelGGL(nvfp4_amax_kernel, dim3((unsigned)ablocks), dim3(256), 0, stream,
                        static_cast<const u32x4*>(X), nvec, slot);
