@@ -92,11 +92,35 @@ __global__ __launch_bounds__(256) void nvfp4_quant_kernel(const u32x4* __restric
     const float D = __builtin_amdgcn_cvt_f32_fp8((int)sb, 0) * g;
     const uint32_t w[4] = {v.x, v.y, v.z, v.w};
     uint32_t packed = 0;
+    if (D >= 0x1p-100f && D <= 0x1p100f) {
+        // y = fl32(x / D) without a divide per element: r = 1/D correctly rounded (one IEEE
+        // divide per lane), q = x*r, then Markstein's correction with the exact remainder
+        // x - q*D gives the correctly rounded quotient (Markstein's theorem: r within half an
+        // ulp of 1/D and q within one ulp of x/D; with the range guard, r and q stay normal
+        // and the remainder is exact wherever x/D is near an E2M1 rounding boundary, since
+        // the block scale keeps |x| < 9*D).  The E2M1 code is
+        // then the hardware convert at unit scale, which applies exactly the nearest-even,
+        // saturating rule (checked against it on every finite fp32 input).
+        const float r = 1.0f / D;
+        float y[8];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-        const uint32_t b = (e & 1) ? (w[e >> 1] & 0xFFFF0000u) : (w[e >> 1] << 16);
-        const uint32_t c = D == 0.0f ? ((b >> 28) & 8u) : e2m1_code(__uint_as_float(b) / D);
-        packed |= c << (4 * e);
+        for (int e = 0; e < 8; ++e) {
+            const float x = __uint_as_float((e & 1) ? (w[e >> 1] & 0xFFFF0000u) : (w[e >> 1] << 16));
+            const float q = x * r;
+            // negated remainder q*D - x, so that x = -0 keeps its sign: y = -0
+            y[e] = __builtin_fmaf(-__builtin_fmaf(q, D, -x), r, q);
+        }
+        packed = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(packed, y[0], y[1], 1.0f, 0);
+        packed = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(packed, y[2], y[3], 1.0f, 1);
+        packed = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(packed, y[4], y[5], 1.0f, 2);
+        packed = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(packed, y[6], y[7], 1.0f, 3);
+    } else {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const uint32_t b = (e & 1) ? (w[e >> 1] & 0xFFFF0000u) : (w[e >> 1] << 16);
+            const uint32_t c = D == 0.0f ? ((b >> 28) & 8u) : e2m1_code(__uint_as_float(b) / D);
+            packed |= c << (4 * e);
+        }
     }
     if (i < nvec) {
         Xq[i] = packed;

@@ -16,6 +16,23 @@ def pytest_configure(config):
 
 
 @pytest.fixture(scope="session")
+def markstein_lib():
+    """Build the test-side check of the NVFP4 coder's division (tests/helpers/markstein_div.c)."""
+    import ctypes
+    src = os.path.join(ROOT, "tests", "helpers", "markstein_div.c")
+    out = os.path.join(tempfile.mkdtemp(prefix="fgq_helpers_"), "libmarkstein.so")
+    subprocess.check_call(["gcc", "-O2", "-std=gnu99", "-ffp-contract=off", "-fno-fast-math",
+                           "-fPIC", "-shared", src, "-o", out, "-lm"])
+    lib = ctypes.CDLL(out)
+    lib.markstein_sweep.restype = ctypes.c_uint64
+    lib.markstein_sweep.argtypes = [ctypes.c_uint64, ctypes.c_uint64,
+                                    ctypes.POINTER(ctypes.c_uint64),
+                                    ctypes.POINTER(ctypes.c_uint64),
+                                    ctypes.POINTER(ctypes.c_uint64)]
+    return lib
+
+
+@pytest.fixture(scope="session")
 def helper_lib():
     """Build the test-side helper C code (independent of the oracle) into a temp dir."""
     import ctypes
