@@ -17,9 +17,11 @@
 //   * the scale is applied by one v_fma_f32 per output element per chunk,
 //     acc = fma(P, sA*sB, acc);
 //   * A/B chunks are staged in LDS as E4M3 bytes, double-buffered, filled by
-//     global_load_lds_dwordx4 (direct to LDS, no VGPR staging); 16-byte columns are
-//     XOR-swizzled by row so that fragment reads spread over the banks; operands are
-//     converted to f16 in registers after the LDS read (v_cvt_scalef32_pk_f16_fp8);
+//     global_load_lds_dwordx4 (direct to LDS, no VGPR staging), the refill of one stage
+//     issued a few loads at a time between the column blocks of the other's compute;
+//     16-byte columns are XOR-swizzled by row so that fragment reads spread over the banks;
+//     operands are converted to f16 in registers after the LDS read
+//     (v_cvt_scalef32_pk_f16_fp8);
 //   * B stays N-contiguous in LDS; its operand (one column, consecutive k per lane) is
 //     gathered by ds_read_b64_tr_b8, which transposes an 8(k) x 16(n) byte block across
 //     each 16-lane group;
