@@ -344,8 +344,18 @@ def main():
         b.record(stream)
     torch.cuda.synchronize()
     mfma_ceiling = cal_flops / (float(np.median([a.elapsed_time(b) for a, b in cev])) * 1e-3) / 1e12
+    # the same for the FP8 MFMAs (16x16x128 f8f6f4), which the GEMM does not use: what the
+    # FP8 matrix cores reach here, for context next to the 5.0 PFLOP/s datasheet peak
+    fgq.fgq_calib_mfma_fp8(cal_out, 2 * ncu, cal_iters // 2, stream)
+    for a, b in cev:
+        a.record(stream)
+        cal_flops8 = fgq.fgq_calib_mfma_fp8(cal_out, 2 * ncu, cal_iters // 2, stream)
+        b.record(stream)
+    torch.cuda.synchronize()
+    mfma8_ceiling = cal_flops8 / (float(np.median([a.elapsed_time(b) for a, b in cev])) * 1e-3) / 1e12
     del cal_out
-    log(f"MFMA-only ceiling (16x16x32 f16): {mfma_ceiling:.0f} TFLOP/s")
+    log(f"MFMA-only ceilings: 16x16x32 f16 {mfma_ceiling:.0f}, 16x16x128 fp8 "
+        f"{mfma8_ceiling:.0f} TFLOP/s")
     log(f"step {ms_per_step:.4f} ms | quant A {qa_ms*1e3:.1f} us  quant B {qw_ms*1e3:.1f} us  "
         f"GEMM {gm_ms*1e3:.1f} us = {gemm_tflops:.0f} TFLOP/s")
 
@@ -546,6 +556,7 @@ def main():
             "min_us": round(float(gm_all.min()) * 1e3, 2),
             "mfma_only_ceiling": round(mfma_ceiling, 1),
             "frac_of_mfma_only_ceiling": round(gemm_tflops / mfma_ceiling, 4),
+            "fp8_mfma_only_ceiling": round(mfma8_ceiling, 1),
             "note": "partials use f16 MFMAs on exactly converted E4M3 operands (gfx950 FP8 "
                     "MFMA accumulation is too coarse for the fp32 tolerance); frac_f16_peak "
                     "is against the 2500 TFLOP/s dense f16 peak of that instruction",

@@ -20,7 +20,13 @@ bool overlap(const void* a, int64_t na, const void* b, int64_t nb)
     return pa < pb + (uintptr_t)nb && pb < pa + (uintptr_t)na;
 }
 
-int launch_status(hipError_t e) { return e == hipSuccess ? FGQ_OK : FGQ_ERR_LAUNCH; }
+// a grid beyond the dispatch's 32-bit work-item count is refused before launch: a shape error
+int launch_status(hipError_t e)
+{
+    return e == hipSuccess                      ? FGQ_OK
+           : e == hipErrorInvalidConfiguration ? FGQ_ERR_SHAPE
+                                                : FGQ_ERR_LAUNCH;
+}
 
 // argument checks shared by the fp32-scale and UE8M0-scale entry points (ss: bytes per
 // scale); FGQ_OK for a valid call, including an empty one
@@ -294,6 +300,37 @@ int fgq_calib_mfma_f16(float* out, int64_t blocks, int64_t iters, void* stream)
         return FGQ_ERR_ALIGN;
     return launch_status(
         fgq::launch_calib_mfma_f16(out, blocks, iters, static_cast<hipStream_t>(stream)));
+}
+
+int fgq_calib_mfma_fp8(float* out, int64_t blocks, int64_t iters, void* stream)
+{
+    if (blocks < 1 || blocks > (int64_t(1) << 20) || iters < 0 || iters > (int64_t(1) << 24))
+        return FGQ_ERR_SHAPE;
+    if (!out)
+        return FGQ_ERR_NULL;
+    if (misaligned(out))
+        return FGQ_ERR_ALIGN;
+    return launch_status(
+        fgq::launch_calib_mfma_fp8(out, blocks, iters, static_cast<hipStream_t>(stream)));
+}
+
+int fgq_probe_fp8_mfma_partials(const void* A_q, const void* B_q, float* P, int64_t M,
+                                int64_t N, int64_t K, void* stream)
+{
+    if (M < 0 || N < 0 || K < 0 || M % 16 || N % 16 || K % 128 || M > (int64_t(1) << 16) ||
+        N > (int64_t(1) << 16) || K > (int64_t(1) << 16))
+        return FGQ_ERR_SHAPE;
+    if (M == 0 || N == 0 || K == 0)
+        return FGQ_OK;
+    if (!A_q || !B_q || !P)
+        return FGQ_ERR_NULL;
+    if (misaligned(A_q) || misaligned(B_q) || misaligned(P))
+        return FGQ_ERR_ALIGN;
+    const int64_t np = (K / 128) * M * N * 4;
+    if (overlap(P, np, A_q, M * K) || overlap(P, np, B_q, K * N))
+        return FGQ_ERR_ALIAS;
+    return launch_status(fgq::launch_probe_fp8_mfma_partials(A_q, B_q, P, M, N, K,
+                                                             static_cast<hipStream_t>(stream)));
 }
 
 }  // extern "C"

@@ -525,6 +525,8 @@ static hipError_t launch_cfg(const void* A_q, const void* sA_, const void* B_q, 
     const typename SI::T* sB = static_cast<const typename SI::T*>(sB_);
     const int64_t tiles =
         ((M + Cfg::BM - 1) / Cfg::BM) * ((n_end - n_begin + Cfg::BN - 1) / Cfg::BN);
+    if (!grid_fits(tiles, Cfg::NT))
+        return hipErrorInvalidConfiguration;
     if (out_bf16)
         hipLaunchKernelGGL((gemm_fp8_blockscaled_kernel<Cfg, SI, true>), dim3((unsigned)tiles),
                            dim3(Cfg::NT), 0, stream, static_cast<const uint8_t*>(A_q), sA,
@@ -666,6 +668,8 @@ static hipError_t launch_ksplit(const void* A_q, const void* sA_, const void* B_
     const typename SI::T* sA = static_cast<const typename SI::T*>(sA_);
     const typename SI::T* sB = static_cast<const typename SI::T*>(sB_);
     const int64_t tiles = ((M + Cfg::BM - 1) / Cfg::BM) * (N / Cfg::BN);
+    if (!grid_fits(tiles, Cfg::NT * KG))
+        return hipErrorInvalidConfiguration;
     if (out_bf16)
         hipLaunchKernelGGL((gemm_fp8_blockscaled_ksplit_kernel<Cfg, SI, true, KG>),
                            dim3((unsigned)tiles), dim3(Cfg::NT * KG), 0, stream,
@@ -841,6 +845,8 @@ static hipError_t launch_narrow(const void* A_q, const void* sA_, const void* B_
     const typename SI::T* sA = static_cast<const typename SI::T*>(sA_);
     const typename SI::T* sB = static_cast<const typename SI::T*>(sB_);
     const int64_t tiles = ((M + Cfg::BM - 1) / Cfg::BM) * (N / Cfg::BN);
+    if (!grid_fits(tiles, Cfg::NT))
+        return hipErrorInvalidConfiguration;
     if (out_bf16)
         hipLaunchKernelGGL((gemm_fp8_blockscaled_narrow_kernel<Cfg, SI, true>),
                            dim3((unsigned)tiles), dim3(Cfg::NT), 0, stream,
@@ -860,6 +866,8 @@ static hipError_t launch_fused(const void* A_q, const float* sA, const void* B_q
                                hipStream_t stream)
 {
     const int64_t tiles = ((M + Cfg::BM - 1) / Cfg::BM) * ((N + Cfg::BN - 1) / Cfg::BN);
+    if (!grid_fits(tiles, Cfg::NT))
+        return hipErrorInvalidConfiguration;
     hipLaunchKernelGGL((gemm_fp8_blockscaled_kernel<Cfg, ScaleIn<false>, true, true>), dim3((unsigned)tiles),
                        dim3(Cfg::NT), 0, stream, static_cast<const uint8_t*>(A_q), sA,
                        static_cast<const uint8_t*>(B_q), sB, C, M, N, K, (int64_t)0, N,
@@ -932,6 +940,11 @@ static hipError_t launch_gemm(const void* A_q, const void* sA, const void* B_q, 
     if (variant == GEMM_AUTO && M >= 256) {
         const int64_t split = tail_split_column(M, N);
         if (split < N) {
+            const int64_t tiles_l = ((M + CfgLarge::BM - 1) / CfgLarge::BM) * (split / CfgLarge::BN);
+            const int64_t tiles_s =
+                ((M + CfgSmall::BM - 1) / CfgSmall::BM) * ((N - split) / CfgSmall::BN);
+            if (!grid_fits(tiles_l, CfgLarge::NT) || !grid_fits(tiles_s, CfgSmall::NT))
+                return hipErrorInvalidConfiguration;
             const hipError_t e = launch_cfg<CfgLarge, SI>(A_q, sA, B_q, sB, C, M, N, K, out_bf16,
                                                           stream, 0, split);
             if (e != hipSuccess)

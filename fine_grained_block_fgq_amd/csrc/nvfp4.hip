@@ -142,6 +142,8 @@ hipError_t launch_quant_nvfp4(const void* X, void* Xq, uint8_t* sX, float* g, in
 {
     uint32_t* slot = reinterpret_cast<uint32_t*>(g);
     const int64_t nvec = R * C / 8;
+    if (!grid_fits((nvec + 255) / 256, 256))
+        return hipErrorInvalidConfiguration;
     hipLaunchKernelGGL(nvfp4_clear_kernel, dim3(1), dim3(64), 0, stream, slot);
     int64_t ablocks = (nvec + 256 * NVFP4_AMAX_VPT - 1) / (256 * NVFP4_AMAX_VPT);
     ablocks = ablocks < 1 ? 1 : (ablocks > NVFP4_AMAX_BLOCKS ? NVFP4_AMAX_BLOCKS : ablocks);
@@ -361,6 +363,8 @@ static hipError_t launch_nvfp4_cfg(const void* A_q, const uint8_t* sA, const flo
                                    hipStream_t stream)
 {
     const int64_t tiles = ((M + Cfg::BM - 1) / Cfg::BM) * (N / Cfg::BN);
+    if (!grid_fits(tiles, Cfg::NT))
+        return hipErrorInvalidConfiguration;
     if (out_bf16)
         hipLaunchKernelGGL((gemm_nvfp4_kernel<Cfg, true>), dim3((unsigned)tiles), dim3(Cfg::NT),
                            0, stream, static_cast<const uint8_t*>(A_q), sA, gA,

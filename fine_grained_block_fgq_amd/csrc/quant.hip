@@ -131,6 +131,8 @@ static hipError_t launch_act(const void* X, void* Xq, typename Scale::stored_t* 
     int64_t blocks = (T + ACT_TILES_PER_BLOCK - 1) / ACT_TILES_PER_BLOCK;
     if (ACT_GRID > 0 && blocks > ACT_GRID)
         blocks = ACT_GRID;
+    if (!grid_fits(blocks, 64 * ACT_WAVES))
+        return hipErrorInvalidConfiguration;
     hipLaunchKernelGGL(quant_act_1x128_kernel<Scale>, dim3((unsigned)blocks),
                        dim3(64 * ACT_WAVES), 0, stream, static_cast<const u32x4*>(X),
                        static_cast<u32x2*>(Xq), sX, T);
@@ -141,6 +143,8 @@ template <class Scale>
 static hipError_t launch_weight(const void* W, void* Wq, typename Scale::stored_t* sW,
                                 int64_t K, int64_t N, hipStream_t stream)
 {
+    if (!grid_fits(N / 128, WQ_THREADS))
+        return hipErrorInvalidConfiguration;
     hipLaunchKernelGGL(quant_weight_128x128_kernel<Scale>,
                        dim3((unsigned)(N / 128), (unsigned)(K / 128)), dim3(WQ_THREADS), 0,
                        stream, static_cast<const uint8_t*>(W), static_cast<uint8_t*>(Wq), sW,

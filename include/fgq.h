@@ -39,7 +39,9 @@ extern "C" {
 typedef enum {
     FGQ_OK = 0,
     FGQ_ERR_NULL = -1,   /* a required pointer is NULL */
-    FGQ_ERR_SHAPE = -2,  /* negative size, K or N not a multiple of 128, or size too large */
+    FGQ_ERR_SHAPE = -2,  /* negative size, K or N not a multiple of 128, or size too large
+                            (including a launch grid beyond the 2^32 work-items one HIP
+                            dispatch can count; refused before anything is enqueued) */
     FGQ_ERR_ALIGN = -3,  /* a pointer is not 16-byte aligned */
     FGQ_ERR_DTYPE = -4,  /* unknown out_dtype */
     FGQ_ERR_LAUNCH = -5, /* the HIP launch failed (hipGetLastError) */
@@ -202,9 +204,28 @@ int fgq_gemm_nvfp4(const void* A_q, const uint8_t* scale_A, const float* global_
  * blocks * 8 * iters * 16 MFMAs of 16384 flop each.  `out` (device, blocks*512 floats) gets
  * a checksum per thread.  Errors: FGQ_ERR_SHAPE (blocks outside [1, 2^20] or iters outside
  * [0, 2^24]), FGQ_ERR_NULL, FGQ_ERR_ALIGN.
+ *
+ * fgq_calib_mfma_fp8: the same with FP8 (E4M3) MFMAs (v_mfma_f32_16x16x128_f8f6f4): what the
+ * FP8 matrix cores reach.  Work: blocks * 8 * iters * 16 MFMAs of 65536 flop each.  Same
+ * arguments and errors as fgq_calib_mfma_f16.
+ *
+ * fgq_probe_fp8_mfma_partials: the 128-K chunk partials P[kb][m][n] = sum over the chunk of
+ * A_q[m,k] * B_q[k,n], each formed by one FP8 MFMA (v_mfma_f32_16x16x128_f8f6f4) per 16x16
+ * tile, unscaled.  It shows how far the FP8 matrix cores' own sum is from the exact one (page
+ * "Fine-Grained FP8/FP4 Quantization", section "Hopper: CUDA Core Promotion (Nc=128)": the
+ * FP8 tensor-core sum is kept at reduced precision, hence the promotion every 128 K); the GEMM
+ * entry points do not use it.
+ *   A_q  in: device, E4M3 [M, K] row-major, 16-byte aligned
+ *   B_q  in: device, E4M3 [K, N] row-major (N contiguous)
+ *   P    out: device, fp32 [K/128, M, N], overwritten
+ * M and N multiples of 16, K of 128, each at most 65536; any of them 0: no-op.
+ * Errors: FGQ_ERR_SHAPE, FGQ_ERR_NULL, FGQ_ERR_ALIGN, FGQ_ERR_ALIAS (P overlaps an input).
  */
 int fgq_calib_stream(const void* src, void* dst, int64_t n16, void* stream);
 int fgq_calib_mfma_f16(float* out, int64_t blocks, int64_t iters, void* stream);
+int fgq_calib_mfma_fp8(float* out, int64_t blocks, int64_t iters, void* stream);
+int fgq_probe_fp8_mfma_partials(const void* A_q, const void* B_q, float* P, int64_t M,
+                                int64_t N, int64_t K, void* stream);
 
 /* Static text for a status code. */
 const char* fgq_status_string(int status);

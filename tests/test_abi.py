@@ -164,6 +164,31 @@ def test_nvfp4_validation(fn, args, want):
     ("fgq_calib_mfma_f16", (P, 4, -1), -2),
     ("fgq_calib_mfma_f16", (None, 4, 10), -1),
     ("fgq_calib_mfma_f16", (P + 4, 4, 10), -3),
+    ("fgq_calib_mfma_fp8", (P, 0, 10), -2),
+    ("fgq_calib_mfma_fp8", (None, 4, 10), -1),
+    ("fgq_calib_mfma_fp8", (P + 4, 4, 10), -3),
+    ("fgq_probe_fp8_mfma_partials", (P, Q, R, 8, 16, 128), -2),      # M % 16
+    ("fgq_probe_fp8_mfma_partials", (P, Q, R, 16, 16, 64), -2),      # K % 128
+    ("fgq_probe_fp8_mfma_partials", (P, Q, R, 16, 16, 1 << 17), -2),  # too large
+    ("fgq_probe_fp8_mfma_partials", (P, None, R, 16, 16, 128), -1),
+    ("fgq_probe_fp8_mfma_partials", (P + 8, Q, R, 16, 16, 128), -3),
+    ("fgq_probe_fp8_mfma_partials", (P, Q, P + 64, 16, 16, 128), -6),  # P inside A_q
+    ("fgq_probe_fp8_mfma_partials", (None, None, None, 0, 16, 128), 0),
 ])
 def test_calib_validation(fn, args, want):
     assert getattr(fgq.load(), fn)(*args, None) == want
+
+
+# Shapes that pass the argument checks but whose grid would exceed the 2^32 work-items one
+# HIP dispatch can count: refused as shape errors before any launch (the fake addresses are
+# far enough apart that no range overlaps).
+T40, T41, T42 = 1 << 40, 1 << 41, 1 << 42
+
+
+def test_grid_limit_is_a_shape_error():
+    lib = fgq.load()
+    # activation quantizer: 2^20 x 2^17 elements -> 2^33 work-items
+    assert lib.fgq_quantize_act_1x128(P, T40, T41, 1 << 20, 1 << 17, None) == -2
+    # skinny GEMM: 2^23 tiles of 768 threads
+    assert lib.fgq_gemm_fp8_blockscaled_variant(P, 0x40000, T40, 0x100000, T42, 128, 1 << 28,
+                                                128, 0, 4, None) == -2
