@@ -954,13 +954,18 @@ static hipError_t launch_gemm(const void* A_q, const void* sA, const void* B_q, 
         }
     }
     if (variant == GEMM_AUTO) {
-        // wide tiles while they fill the 256 CUs at least once, else narrow tiles
+        // wide tiles while they fill the 256 CUs at least once; else the narrow tiles (one
+        // workgroup per CU, each wave a whole tile over its own chunks: no operand converted
+        // twice) while they fit in one round of the CUs; past that, for M <= 128, the skinny
+        // tiles (half as many workgroups, K split over wave groups)
         const int64_t tiles_large = ((M + CfgLarge::BM - 1) / CfgLarge::BM) * (N / CfgLarge::BN);
         const int64_t tiles_small = ((M + CfgSmall::BM - 1) / CfgSmall::BM) * (N / CfgSmall::BN);
-        variant = (M >= 256 && tiles_large >= 256) ? GEMM_WIDE_256x128
-                  : tiles_small >= 256             ? GEMM_WIDE_128x128
-                  : M <= 128                       ? GEMM_SKINNY
-                                                   : GEMM_NARROW;
+        const int64_t tiles_narrow = ((M + CfgNarrow::BM - 1) / CfgNarrow::BM) * (N / CfgNarrow::BN);
+        const int cus = device_cus();
+        variant = (M >= 256 && tiles_large >= 256)           ? GEMM_WIDE_256x128
+                  : tiles_small >= 256                       ? GEMM_WIDE_128x128
+                  : M <= 128 && tiles_narrow > (cus > 0 ? cus : 256) ? GEMM_SKINNY
+                                                             : GEMM_NARROW;
     }
     switch (variant) {
     case GEMM_WIDE_256x128:
