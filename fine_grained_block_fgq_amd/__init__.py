@@ -20,7 +20,7 @@ __all__ = [
     "fgq_quantize_act_1x128_ue8m0", "fgq_quantize_weight_128x128_ue8m0",
     "fgq_gemm_fp8_blockscaled_ue8m0", "fgq_quantize_nvfp4", "fgq_gemm_nvfp4", "FGQ_OUT_F32", "FGQ_OUT_BF16", "FGQ_GEMM_AUTO",
     "FGQ_GEMM_WIDE_256x128", "FGQ_GEMM_WIDE_128x128", "FGQ_GEMM_NARROW_64x32",
-    "FGQ_GEMM_SKINNY_128x32", "fgq_calib_stream", "fgq_calib_mfma_f16",
+    "FGQ_GEMM_SKINNY_128x32", "FGQ_GEMM_NARROW_64x64", "fgq_calib_stream", "fgq_calib_mfma_f16",
     "fgq_calib_mfma_fp8", "fgq_probe_fp8_mfma_partials",
 ]
 
@@ -28,7 +28,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_HERE, "libfgq.so")
 FGQ_OUT_F32, FGQ_OUT_BF16 = 0, 1
 FGQ_GEMM_AUTO, FGQ_GEMM_WIDE_256x128, FGQ_GEMM_WIDE_128x128, FGQ_GEMM_NARROW_64x32 = 0, 1, 2, 3
-FGQ_GEMM_SKINNY_128x32 = 4
+FGQ_GEMM_SKINNY_128x32, FGQ_GEMM_NARROW_64x64 = 4, 5
 _lib = None
 
 

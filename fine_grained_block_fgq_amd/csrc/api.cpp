@@ -70,14 +70,15 @@ int check_gemm(const void* A_q, const void* scale_A, const void* B_q, const void
 {
     if (out_dtype != FGQ_OUT_F32 && out_dtype != FGQ_OUT_BF16)
         return FGQ_ERR_DTYPE;
-    if (variant < FGQ_GEMM_AUTO || variant > FGQ_GEMM_SKINNY_128x32)
+    if (variant < FGQ_GEMM_AUTO || variant > FGQ_GEMM_NARROW_64x64)
         return FGQ_ERR_VARIANT;
     if (M < 0 || N < 0 || K < 0 || K % 128 != 0 || N % 128 != 0 || M > kMaxDim ||
         N > kMaxDim || K > kMaxDim)
         return FGQ_ERR_SHAPE;
     if (((M + 127) / 128) * (N / 128) > kMaxDim)
         return FGQ_ERR_SHAPE;
-    if ((variant == FGQ_GEMM_NARROW_64x32 && ((M + 63) / 64) * (N / 32) > kMaxDim) ||
+    if (((variant == FGQ_GEMM_NARROW_64x32 || variant == FGQ_GEMM_NARROW_64x64) &&
+         ((M + 63) / 64) * (N / 32) > kMaxDim) ||
         (variant == FGQ_GEMM_SKINNY_128x32 && ((M + 127) / 128) * (N / 32) > kMaxDim))
         return FGQ_ERR_SHAPE;
     if (M == 0 || N == 0)

@@ -29,7 +29,8 @@ enum GemmVariant {
     GEMM_WIDE_256x128 = 1,
     GEMM_WIDE_128x128 = 2,
     GEMM_NARROW = 3,
-    GEMM_SKINNY = 4
+    GEMM_SKINNY = 4,
+    GEMM_NARROW_64x64 = 5
 };
 
 // out_bf16: 0 -> C is fp32, 1 -> C is bf16 (nearest-even)

@@ -92,13 +92,18 @@ struct GemmCfg {
         // cover 32 banks, and bit 5 of k separates the two groups read in the same cycle
         if (B_CHUNKS == 2)
             return (k >> 5) & 1;
+        // BN = 64: four rows per 256-byte bank line; bit 2 and bit 5 of k separate the 16
+        // rows read in one cycle
+        if (B_CHUNKS == 4)
+            return ((k >> 2) & 1) | (((k >> 5) & 1) << 1);
         return B_CHUNKS == 8 ? (((k >> 1) & 3) | (((k >> 5) & 1) << 2))
                              : ((k & 7) | (((k >> 5) & 1) << 3));
 #else
         return k & 7;
 #endif
     }
-    static_assert(B_CHUNKS == 2 || B_CHUNKS == 8 || B_CHUNKS == 16, "BN is 32, 128 or 256");
+    static_assert(B_CHUNKS == 2 || B_CHUNKS == 4 || B_CHUNKS == 8 || B_CHUNKS == 16,
+                  "BN is 32, 64, 128 or 256");
     // waits: every wave issues this many direct-to-LDS loads per stage (S loads go to the
     // first S_LOADS waves); the pipeline waits with the smallest count, which is safe.
     static constexpr int MIN_LOADS = (A_LOADS + B_LOADS) / NW;
@@ -691,11 +696,12 @@ static hipError_t launch_ksplit(const void* A_q, const void* sA_, const void* B_
 // The KW partial tiles are summed in LDS in wave order ((w0 + w1) + w2) + ..., a fixed
 // order, so results are deterministic.  The per-chunk arithmetic is that of the wide
 // kernel: f16 MFMA partials over the 128-K chunk, then acc = fma(P, sA*sB, acc).
-template <int BM_, int KW_, int STAGES_>
+template <int BM_, int KW_, int STAGES_, int BN_ = 32>
 struct NarrowCfg {
-    static constexpr int BM = BM_, BN = 32, KW = KW_, STAGES = STAGES_;
+    static constexpr int BM = BM_, BN = BN_, KW = KW_, STAGES = STAGES_;
     static constexpr int NT = 64 * KW;
-    static constexpr int FM = BM / 16, FN = 2;
+    static constexpr int FM = BM / 16, FN = BN / 16;
+    static constexpr int B_CHUNKS = BN / 16, B_ROWS_PER_LOAD = 1024 / BN;
     static constexpr int A_BYTES = BM * 128, B_BYTES = 128 * BN, S_BYTES = 256;
     static constexpr int STAGE = A_BYTES + B_BYTES + S_BYTES;
     // the bf16 tile staged for the epilogue: rows of BN values plus 16 bytes
@@ -708,18 +714,25 @@ struct NarrowCfg {
                                          ? KW * STAGES * STAGE
                                          : KW * BM * RED_LD * 4;
     static_assert(BM == 32 || BM == 64, "tile rows");
+    static_assert(BN == 32 || BN == 64, "tile columns");
     static_assert(STAGES == 2 || STAGES == 3, "LDS ring depth");
     static_assert(LDS_BYTES <= 160 * 1024, "LDS capacity (160 KB per CU)");
-    static_assert(LOADS < 16, "wait count range");
-    // A: same row swizzle as the wide kernel.  B rows are 32 bytes (two 16-byte halves);
-    // the half is XORed with bit 5 of k, so the two 16-lane groups of one transposed read
-    // (k and k+32) fall on disjoint banks.
+    static_assert(LOADS < 64, "wait count range");
+    // A: same row swizzle as the wide kernel.  B rows of 32 bytes (two 16-byte chunks): the
+    // chunk is XORed with bit 5 of k, so the two 16-lane groups of one transposed read (k and
+    // k+32) fall on disjoint banks.  B rows of 64 bytes (four chunks, four rows per 256-byte
+    // bank line): the chunk is XORed with bit 2 of k and bit 5 of k, so the 16 rows one
+    // transposed read serves per cycle (8t..8t+7 and 32+8t..32+8t+7) take 16 distinct
+    // 16-byte bank slots.
     static __device__ __forceinline__ int a_swz(int row) { return (row >> 1) & 7; }
-    static __device__ __forceinline__ int b_swz(int k) { return (k >> 5) & 1; }
+    static __device__ __forceinline__ int b_swz(int k)
+    {
+        return BN == 32 ? (k >> 5) & 1 : ((k >> 2) & 1) | (((k >> 5) & 1) << 1);
+    }
 };
 
 // one wave fills its stage with chunk kb: A rows m0..m0+BM-1, B rows of the chunk for
-// columns n0..n0+31, and scale_A of the rows
+// columns n0..n0+BN-1, and scale_A of the rows
 template <class Cfg, class SI>
 __device__ __forceinline__ void narrow_load(uint8_t LDS* stage, const uint8_t* __restrict__ A,
                                             const typename SI::T* __restrict__ sA,
@@ -735,10 +748,12 @@ __device__ __forceinline__ void narrow_load(uint8_t LDS* stage, const uint8_t* _
         gm = gm < M ? gm : M - 1;
         dma_b128(A + gm * K + kb * 128 + c * 16, lds_addr(stage + u * 1024));
     }
+    // B: instruction u covers k rows u*R..u*R+R-1 (R = 1024/BN); lane -> row u*R +
+    // lane/(BN/16), physical 16-byte column lane%(BN/16) holding logical column p ^ swz(k)
 #pragma unroll
     for (int u = 0; u < Cfg::B_LOADS; ++u) {
-        const int k = u * 32 + (lane >> 1);
-        const int c = (lane & 1) ^ Cfg::b_swz(k);
+        const int k = u * Cfg::B_ROWS_PER_LOAD + lane / Cfg::B_CHUNKS;
+        const int c = (lane % Cfg::B_CHUNKS) ^ Cfg::b_swz(k);
         dma_b128(B + (kb * 128 + k) * N + n0 + c * 16,
                  lds_addr(stage + Cfg::A_BYTES + u * 1024));
     }
@@ -887,6 +902,10 @@ using CfgSmall = GemmCfg<FGQ_SMALL_CFG>;
 #define FGQ_NARROW_CFG 64, 4, 2
 #endif
 using CfgNarrow = NarrowCfg<FGQ_NARROW_CFG>;
+#ifndef FGQ_NARROW64_CFG
+#define FGQ_NARROW64_CFG 64, 4, 2, 64
+#endif
+using CfgNarrow64 = NarrowCfg<FGQ_NARROW64_CFG>;
 #ifndef FGQ_SKINNY_CFG
 #define FGQ_SKINNY_CFG 128, 32, 4, 1, 2
 #endif
@@ -954,18 +973,25 @@ static hipError_t launch_gemm(const void* A_q, const void* sA, const void* B_q, 
         }
     }
     if (variant == GEMM_AUTO) {
-        // wide tiles while they fill the 256 CUs at least once; else the narrow tiles (one
-        // workgroup per CU, each wave a whole tile over its own chunks: no operand converted
-        // twice) while they fit in one round of the CUs; past that, for M <= 128, the skinny
-        // tiles (half as many workgroups, K split over wave groups)
+        // Wide tiles while they fill the 256 CUs at least once.  Below that (measured back to
+        // back over M = 1..640, N = 256..7168, K = 256..4096): the narrow 64x32 tiles (one
+        // workgroup per CU, each wave a whole tile over its own chunks, so no operand is
+        // converted twice) while they fit one round of the CUs; else the narrow 64x64 tiles
+        // (half the workgroups, each operand still converted once) while they fit two rounds,
+        // except for M <= 128 with at most two K chunks, where the skinny tiles are quicker;
+        // else 128x128 wide tiles (one round).
         const int64_t tiles_large = ((M + CfgLarge::BM - 1) / CfgLarge::BM) * (N / CfgLarge::BN);
         const int64_t tiles_small = ((M + CfgSmall::BM - 1) / CfgSmall::BM) * (N / CfgSmall::BN);
-        const int64_t tiles_narrow = ((M + CfgNarrow::BM - 1) / CfgNarrow::BM) * (N / CfgNarrow::BN);
-        const int cus = device_cus();
-        variant = (M >= 256 && tiles_large >= 256)           ? GEMM_WIDE_256x128
-                  : tiles_small >= 256                       ? GEMM_WIDE_128x128
-                  : M <= 128 && tiles_narrow > (cus > 0 ? cus : 256) ? GEMM_SKINNY
-                                                             : GEMM_NARROW;
+        const int64_t tiles_n32 = ((M + CfgNarrow::BM - 1) / CfgNarrow::BM) * (N / CfgNarrow::BN);
+        const int64_t tiles_n64 =
+            ((M + CfgNarrow64::BM - 1) / CfgNarrow64::BM) * (N / CfgNarrow64::BN);
+        const int cus = device_cus() > 0 ? device_cus() : 256;
+        variant = (M >= 256 && tiles_large >= 256) ? GEMM_WIDE_256x128
+                  : tiles_small >= 256             ? GEMM_WIDE_128x128
+                  : tiles_n32 <= cus               ? GEMM_NARROW
+                  : M <= 128 && K <= 256           ? GEMM_SKINNY
+                  : tiles_n64 <= 2 * cus           ? GEMM_NARROW_64x64
+                                                   : GEMM_WIDE_128x128;
     }
     switch (variant) {
     case GEMM_WIDE_256x128:
@@ -974,6 +1000,8 @@ static hipError_t launch_gemm(const void* A_q, const void* sA, const void* B_q, 
         return launch_cfg<CfgSmall, SI>(A_q, sA, B_q, sB, C, M, N, K, out_bf16, stream);
     case GEMM_NARROW:
         return launch_narrow<CfgNarrow, SI>(A_q, sA, B_q, sB, C, M, N, K, out_bf16, stream);
+    case GEMM_NARROW_64x64:
+        return launch_narrow<CfgNarrow64, SI>(A_q, sA, B_q, sB, C, M, N, K, out_bf16, stream);
     case GEMM_SKINNY:
         return launch_ksplit<CfgSkinny, SI, FGQ_SKINNY_KG>(A_q, sA, B_q, sB, C, M, N, K, out_bf16,
                                                            stream);

@@ -97,26 +97,28 @@ int fgq_gemm_fp8_blockscaled(const void* A_q, const float* scale_A, const void* 
  * Kernel families of the GEMM.  Every variant computes the same function within the same
  * tolerance; they differ in tiling:
  *   WIDE_256x128 / WIDE_128x128: one workgroup per output tile, K walked in order;
- *   NARROW_64x32: 64x32 tiles whose K chunks are split over the 4 waves of a workgroup
- *                 and summed in a fixed order, for shapes with few output tiles;
- *   SKINNY_128x32: 128x32 tiles (4 waves of 32x32) with a 4-deep LDS ring, for M <= 128
- *                 (decode-like): one workgroup per 32 output columns.
- * FGQ_GEMM_AUTO picks from the shape (wide while the wide tiles cover every CU, else skinny
- * for M <= 128, else narrow); it is what fgq_gemm_fp8_blockscaled uses.
+ *   NARROW_64x32 / NARROW_64x64: 64x32 or 64x64 tiles whose K chunks are split over the 4
+ *                 waves of a workgroup (each wave the whole tile over its own chunks) and
+ *                 summed in a fixed order, for shapes with few output tiles;
+ *   SKINNY_128x32: 128x32 tiles, 12 waves in three groups of four (32x32 each) that split
+ *                 the K chunks, summed in a fixed order, for M <= 128 (decode-like).
+ * FGQ_GEMM_AUTO picks from the shape (wide while the wide tiles cover every CU, else one of
+ * the narrow and skinny families); it is what fgq_gemm_fp8_blockscaled uses.
  */
 typedef enum {
     FGQ_GEMM_AUTO = 0,
     FGQ_GEMM_WIDE_256x128 = 1,
     FGQ_GEMM_WIDE_128x128 = 2,
     FGQ_GEMM_NARROW_64x32 = 3,
-    FGQ_GEMM_SKINNY_128x32 = 4
+    FGQ_GEMM_SKINNY_128x32 = 4,
+    FGQ_GEMM_NARROW_64x64 = 5
 } fgq_gemm_variant;
 
 /*
  * fgq_gemm_fp8_blockscaled with an explicit kernel family (for tests and tuning).
  * Arguments, requirements and errors as fgq_gemm_fp8_blockscaled; in addition an unknown
- * `variant` gives FGQ_ERR_VARIANT, and NARROW_64x32 / SKINNY_128x32 require
- * ceil(M/64) * (N/32) / ceil(M/128) * (N/32) below 2^31.
+ * `variant` gives FGQ_ERR_VARIANT, and NARROW_64x32 / NARROW_64x64 / SKINNY_128x32 require
+ * ceil(M/64) * (N/32) / ceil(M/64) * (N/64) / ceil(M/128) * (N/32) below 2^31.
  */
 int fgq_gemm_fp8_blockscaled_variant(const void* A_q, const float* scale_A, const void* B_q,
                                      const float* scale_B, void* C, int64_t M, int64_t N,

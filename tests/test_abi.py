@@ -90,7 +90,7 @@ def test_gemm_validation(args, want):
 
 
 @pytest.mark.parametrize("args,want", [
-    ((P, S1, Q, S2, R, 4, 128, 128, 0, 5), -7),     # unknown variant
+    ((P, S1, Q, S2, R, 4, 128, 128, 0, 6), -7),     # unknown variant
     ((P, S1, Q, S2, R, 4, 128, 128, 0, -1), -7),
     ((P, S1, Q, S2, R, 4, 128, 128, 2, 3), -4),     # dtype checked first
     ((P, S1, Q, S2, R, 4, 100, 128, 0, 3), -2),

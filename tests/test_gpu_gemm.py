@@ -15,7 +15,7 @@ from tests.gpu_util import free, gemm_error_ratio, gpu_gemm, log
 pytestmark = pytest.mark.gpu
 
 # every kernel family on every edge shape (0 = the automatic choice)
-VARIANTS = [0, 1, 2, 3, 4]
+VARIANTS = [0, 1, 2, 3, 4, 5]
 
 
 def random_operands(M, N, K, seed):
@@ -64,7 +64,7 @@ def test_tiny_workload_full():
     assert r <= 1.0
 
 
-@pytest.mark.parametrize("variant", [None, 2, 3, 4])
+@pytest.mark.parametrize("variant", [None, 2, 3, 4, 5])
 def test_skinny_workload_full(variant):
     Aq, sA, Bq, sB = workload_operands("skinny")
     log(f"gemm skinny 128x7168x2048 f32 variant={variant}")

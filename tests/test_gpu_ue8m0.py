@@ -127,7 +127,7 @@ def random_e8_operands(M, N, K, seed):
     (64, 1024, 1152), (33, 128, 0),
 ])
 @pytest.mark.parametrize("out", ["f32", "bf16"])
-@pytest.mark.parametrize("variant", [0, 1, 2, 3, 4])
+@pytest.mark.parametrize("variant", [0, 1, 2, 3, 4, 5])
 def test_gemm_edge_shapes(M, N, K, out, variant):
     Aq, eA, Bq, eB = random_e8_operands(M, N, K, seed=M + 3 * N + 5 * K)
     C = gpu_gemm_e8(Aq, eA, Bq, eB, torch.float32 if out == "f32" else torch.bfloat16, variant)
