@@ -189,9 +189,24 @@ def quant_weight_bytes(K, N):
     return 2 * K * N + K * N + 4 * (K // 128) * (N // 128)
 
 
-def cpu_baseline(A, B):
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
+def cpu_baseline(A, B, step_out=None):
     """The oracle as it stands (scalar C, all host threads over independent rows) on the
-    4096^3 workload: quantize A and B, then the fp64 GEMM for all rows."""
+    4096^3 workload: quantize A and B, then the fp64 GEMM for all rows.  With the GPU step's
+    own outputs (codes, scales, bf16 C, computed on the GPU from the same bf16 inputs), the
+    same run also reports their agreement with the oracle's: codes and scales bit for bit,
+    and the largest GEMM error as a fraction of the tolerance 1e-5*sum|ab| + 1e-6 (+ one bf16
+    ulp of the reference)."""
     import oracle
     nt = oracle.threads()
     t0 = time.perf_counter()
@@ -200,8 +215,20 @@ def cpu_baseline(A, B):
     t1 = time.perf_counter()
     M, K = A.shape
     N = B.shape[1]
-    oracle.gemm_f64(Aq, sA, Bq, sB, nt)
+    C_ref, S = oracle.gemm_f64(Aq, sA, Bq, sB, nt)
     t2 = time.perf_counter()
+    parity = None
+    if step_out is not None:
+        gAq, gsA, gBq, gsB, gC = step_out
+        tol = 1e-5 * S + 1e-6
+        mag = np.maximum(np.abs(C_ref) + tol, 2.0 ** -126)
+        tol = tol + 2.0 ** (np.floor(np.log2(mag)) - 7)          # one bf16 ulp
+        parity = {
+            "codes_bit_exact": bool(np.array_equal(gAq, Aq) and np.array_equal(gBq, Bq)),
+            "scales_bit_exact": bool(np.array_equal(gsA.view(np.uint32), sA.view(np.uint32))
+                                     and np.array_equal(gsB.view(np.uint32), sB.view(np.uint32))),
+            "gemm_max_error_over_tolerance": float(np.max(np.abs(gC - C_ref) / tol)),
+        }
     return {
         "value": 2.0 * M * N * K / (t2 - t1) / 1e12,
         "unit": "TFLOP/s",
@@ -212,6 +239,8 @@ def cpu_baseline(A, B):
                   f"/ GEMM time",
         "quantize_GBps": (quant_act_bytes(M, K) + quant_weight_bytes(K, N)) / (t1 - t0) / 1e9,
         "seconds": t2 - t0,
+        "cpu_model": cpu_model(),
+        "parity_of_the_gpu_step": parity,
     }
 
 
@@ -315,6 +344,10 @@ def main():
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     ms_per_step = (t1 - t0) * 1e3 / args.steps
+    # the step's outputs, for the oracle comparison of the cpu_baseline leg
+    step_out = None if args.no_cpu_baseline else [
+        Aq.cpu().numpy(), sA.cpu().numpy(), Bq.cpu().numpy(), sB.cpu().numpy(),
+        C.float().cpu().numpy().astype(np.float64)]
     gm_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in evs]))
     # the two quantizers of the step, each between its own events (outside the timed steps)
     qev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(50)]
@@ -332,7 +365,8 @@ def main():
     gemm_tflops = flops / (gm_ms * 1e-3) / 1e12
     # measured ceiling: f16 MFMAs only (the partials' instruction), two waves per SIMD on
     # every CU, ~1 ms per launch, at the same (warm) clock
-    ncu = torch.cuda.get_device_properties(dev).multi_processor_count
+    props = torch.cuda.get_device_properties(dev)
+    ncu = props.multi_processor_count
     cal_out = torch.empty((2 * ncu * 512,), dtype=torch.float32, device=dev)
     cal_iters = 2000
     fgq.fgq_calib_mfma_f16(cal_out, 2 * ncu, cal_iters, stream)
@@ -551,6 +585,9 @@ def main():
         "config": {"workload": "4096^3 step: quantize A 1x128 + quantize B 128x128 + "
                                "block-scaled FP8 GEMM, bf16 C",
                    "M": M, "N": N, "K": K, "out": "bf16"},
+        "device": {"name": props.name, "arch": getattr(props, "gcnArchName", None),
+                   "compute_units": props.multi_processor_count,
+                   "memory_GiB": round(props.total_memory / 2**30, 1)},
         "roofline": {
             "bound": "mfma",
             "kernel": "gemm_fp8_blockscaled_kernel 4096^3 bf16 out",
@@ -615,7 +652,7 @@ def main():
     }
     if not args.no_cpu_baseline:
         log("timing the CPU oracle on the 4096^3 workload")
-        out["cpu_baseline"] = cpu_baseline(A_bits, B_bits)
+        out["cpu_baseline"] = cpu_baseline(A_bits, B_bits, step_out)
     print(json.dumps(out), flush=True)
 
 
