@@ -177,6 +177,69 @@ def summarize(ktrace_dir, fetch_dir, write_dir, mfma_dir=None):
     print("\n".join(out))
 
 
+# two rocprofv3 --pmc passes over `bench.py --mode profile` (8 SQ counters and one GRBM
+# counter each, the most one pass collects)
+SQ_PASSES = [
+    "SQ_WAVE_CYCLES SQ_BUSY_CYCLES SQ_WAIT_ANY SQ_WAIT_INST_ANY SQ_ACTIVE_INST_VALU "
+    "SQ_VALU_MFMA_BUSY_CYCLES SQ_VALU_MFMA_COEXEC_CYCLES SQ_INSTS_VALU GRBM_GUI_ACTIVE",
+    "SQ_INSTS_MFMA SQ_INSTS_VALU_CVT SQ_INSTS_LDS SQ_INSTS_SALU SQ_ACTIVE_INST_LDS "
+    "SQ_LDS_BANK_CONFLICT SQ_LDS_IDX_ACTIVE SQ_ACTIVE_INST_ANY GRBM_GUI_ACTIVE",
+]
+
+
+def summarize_sq(dirs):
+    """Instruction mix and unit activity of the 4096^3 GEMM dispatch from the SQ counter passes
+    (medians over its dispatches): MFMA busy as a fraction of the 1024 SIMDs' cycles
+    (GRBM_GUI_ACTIVE counts each of the 8 XCDs), instructions per MFMA, and wait / LDS rates."""
+    import csv
+    import glob
+    vals = {}
+    for d in dirs:
+        f = glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True)
+        if not f:
+            raise SystemExit(f"no counter_collection.csv under {d}")
+        with open(f[0]) as fh:
+            for r in csv.DictReader(fh):
+                if "gemm_fp8_blockscaled_kernel" in r["Kernel_Name"] and \
+                        int(r["Grid_Size"]) == 262144 and "ScaleInILb1" not in r["Kernel_Name"]:
+                    vals.setdefault(r["Counter_Name"], []).append(float(r["Counter_Value"]))
+    m = {k: sorted(v)[len(v) // 2] for k, v in vals.items()}
+    need = ["GRBM_GUI_ACTIVE", "SQ_VALU_MFMA_BUSY_CYCLES", "SQ_INSTS_MFMA", "SQ_INSTS_VALU"]
+    if any(k not in m for k in need):
+        raise SystemExit(f"missing counters: {[k for k in need if k not in m]}")
+    xcd_cycles = m["GRBM_GUI_ACTIVE"] / 8
+    mf = m["SQ_INSTS_MFMA"]
+    lines = ["4096^3 GEMM dispatch (gemm_fp8_blockscaled_kernel, 256x128 tiles, bf16 C): "
+             "SQ counters, median over its dispatches",
+             f"{'counter':32s} {'value':>16s}"]
+    lines += [f"{k:32s} {v:16.0f}" for k, v in sorted(m.items())]
+    lines += ["",
+              f"cycles per XCD (GRBM_GUI_ACTIVE/8)       {xcd_cycles:12.0f}",
+              f"MFMA busy / (1024 SIMDs x cycles)        {m['SQ_VALU_MFMA_BUSY_CYCLES'] / (xcd_cycles * 1024):12.3f}",
+              f"VALU instructions per MFMA               {m['SQ_INSTS_VALU'] / mf:12.2f}"]
+    if "SQ_INSTS_VALU_CVT" in m:
+        lines.append(f"conversions per MFMA                     {m['SQ_INSTS_VALU_CVT'] / mf:12.2f}")
+    if "SQ_INSTS_LDS" in m:
+        lines.append(f"LDS instructions per MFMA                {m['SQ_INSTS_LDS'] / mf:12.2f}")
+    if "SQ_VALU_MFMA_COEXEC_CYCLES" in m:
+        lines.append(f"MFMA cycles with a VALU op co-issued     "
+                     f"{m['SQ_VALU_MFMA_COEXEC_CYCLES'] / m['SQ_VALU_MFMA_BUSY_CYCLES']:12.3f}")
+    if "SQ_WAVE_CYCLES" in m:
+        for k in ("SQ_WAIT_ANY", "SQ_WAIT_INST_ANY", "SQ_ACTIVE_INST_VALU"):
+            if k in m:
+                lines.append(f"{k + ' / SQ_WAVE_CYCLES':41s}{m[k] / m['SQ_WAVE_CYCLES']:12.3f}")
+    if "SQ_LDS_IDX_ACTIVE" in m and "SQ_LDS_BANK_CONFLICT" in m:
+        lines.append(f"LDS bank-conflict cycles / LDS active    "
+                     f"{m['SQ_LDS_BANK_CONFLICT'] / m['SQ_LDS_IDX_ACTIVE']:12.3f}")
+    os.makedirs(PROFILES, exist_ok=True)
+    with open(os.path.join(PROFILES, "sq_counters_gemm_4096.txt"), "w") as f:
+        f.write("commands: cd /tmp && export TMPDIR=/tmp; for each counter set P of bench.py's "
+                "SQ_PASSES: rocprofv3 --pmc P -f csv -d <dir> -o run -- python3 bench.py --mode "
+                "profile\nsummary: python3 bench.py --summarize-sq <dir 1> <dir 2>\n\n")
+        f.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
 def to_dev_bf16(bits, torch):
     return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).cuda()
 
@@ -280,6 +343,9 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--summarize", nargs="+", metavar="DIR",
                     help="write profiles/ summaries from rocprofv3 csv output and exit")
+    ap.add_argument("--summarize-sq", nargs="+", metavar="DIR",
+                    help="write profiles/sq_counters_gemm_4096.txt from the SQ counter passes "
+                         "(SQ_PASSES) of --mode profile and exit")
     ap.add_argument("--mode", choices=["bench", "profile"], default="bench",
                     help="profile: a short pass for hardware-counter runs -- the GEMM, both "
                          "quantizers and a plain 512 MiB copy (torch.mul by 1) as the "
@@ -287,6 +353,9 @@ def main():
     args = ap.parse_args()
     if args.summarize:
         summarize(*args.summarize)
+        return
+    if args.summarize_sq:
+        summarize_sq(args.summarize_sq)
         return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: the path has no multi-GPU stage here "
