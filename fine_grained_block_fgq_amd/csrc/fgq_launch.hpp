@@ -14,6 +14,9 @@ inline bool grid_fits(int64_t blocks, int64_t threads)
     return blocks >= 0 && blocks <= kMaxWorkItems / threads;
 }
 
+// compute units of the current device (0 if the query fails); cached per device
+int device_cus();
+
 hipError_t launch_quant_act_1x128(const void* X, void* Xq, float* sX, int64_t M, int64_t K,
                                   hipStream_t stream);
 hipError_t launch_quant_weight_128x128(const void* W, void* Wq, float* sW, int64_t K,

@@ -915,7 +915,7 @@ using CfgNarrow64 = NarrowCfg<FGQ_NARROW64_CFG>;
 using CfgSkinny = GemmCfg<FGQ_SKINNY_CFG>;
 
 // compute units of the current device (queried once per device)
-static int device_cus()
+int device_cus()
 {
     static std::atomic<int> cache[64];
     int dev = 0;

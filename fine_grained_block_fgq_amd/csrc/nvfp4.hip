@@ -257,16 +257,22 @@ __device__ __forceinline__ void fp4_operands(i32x4 raw, uint32_t scale2, f16x8 (
     }
 }
 
-template <class Cfg, bool OUT_BF16>
-__global__ __launch_bounds__(Cfg::NT) void gemm_nvfp4_kernel(
+// KG > 1 (shapes with few output tiles): the workgroup holds KG groups of NW waves; group c
+// takes chunks c, c+KG, ... with its own 2-stage ring, and the KG partial tiles are summed in
+// LDS in group order (a fixed order: results are repeatable bit for bit).
+template <class Cfg, bool OUT_BF16, int KG = 1>
+__global__ __launch_bounds__(Cfg::NT * KG) void gemm_nvfp4_kernel(
     const uint8_t* __restrict__ A, const uint8_t* __restrict__ sA, const float* __restrict__ gA,
     const uint8_t* __restrict__ B, const uint8_t* __restrict__ sB, const float* __restrict__ gB,
     void* __restrict__ Cout, int64_t M, int64_t N, int64_t K)
 {
-    __shared__ __attribute__((aligned(1024))) uint8_t smem_raw[2 * Cfg::STAGE];
-    uint8_t LDS* const smem = (uint8_t LDS*)smem_raw;
+    constexpr int RING = KG * 2 * Cfg::STAGE;
+    constexpr int RED = (KG - 1) * Cfg::NT * Cfg::FM * Cfg::FN * 16;
+    __shared__ __attribute__((aligned(1024))) uint8_t smem_raw[RING > RED ? RING : RED];
     const int lane = threadIdx.x & 63;
-    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int wave_all = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int kg = wave_all / Cfg::NW, wave = wave_all % Cfg::NW;
+    uint8_t LDS* const smem = (uint8_t LDS*)smem_raw + kg * 2 * Cfg::STAGE;
     const int wm = wave / Cfg::WN, wn = wave % Cfg::WN;
     const int g = lane >> 4, q = lane & 15;
 
@@ -304,15 +310,20 @@ __global__ __launch_bounds__(Cfg::NT) void gemm_nvfp4_kernel(
         for (int j = 0; j < Cfg::FN; ++j)
             acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-    if (KB > 0)
-        nvfp4_load<Cfg>(smem, A, sA, B, sB, M, N, K, m0, n0, 0, wave, lane);
-    for (int64_t kb = 0; kb < KB; ++kb) {
-        const uint8_t LDS* cur = smem + (kb & 1) * Cfg::STAGE;
+    // step st: this group's chunk kb = st*KG + kg (when below KB)
+    const int64_t steps = (KB + KG - 1) / KG;
+    if (steps > 0 && kg < KB)
+        nvfp4_load<Cfg>(smem, A, sA, B, sB, M, N, K, m0, n0, kg, wave, lane);
+    for (int64_t st = 0; st < steps; ++st) {
+        const int64_t kb = st * KG + kg;
+        const uint8_t LDS* cur = smem + (st & 1) * Cfg::STAGE;
         wait_vm<0>();
-        lds_barrier();   // chunk kb visible to all; chunk kb-1 fully read
-        if (kb + 1 < KB)
-            nvfp4_load<Cfg>(smem + ((kb + 1) & 1) * Cfg::STAGE, A, sA, B, sB, M, N, K, m0, n0,
-                            kb + 1, wave, lane);
+        lds_barrier();   // step st visible to all; step st-1 fully read
+        if (kb + KG < KB)
+            nvfp4_load<Cfg>(smem + ((st + 1) & 1) * Cfg::STAGE, A, sA, B, sB, M, N, K, m0, n0,
+                            kb + KG, wave, lane);
+        if (kb >= KB)
+            continue;
         f16x8 af[Cfg::FM][4];
 #pragma unroll
         for (int i = 0; i < Cfg::FM; ++i) {
@@ -335,6 +346,32 @@ __global__ __launch_bounds__(Cfg::NT) void gemm_nvfp4_kernel(
         }
     }
 
+    if (KG > 1) {
+        // the KG partial tiles, summed in group order
+        lds_barrier();
+        float LDS* const red = (float LDS*)smem_raw;
+        constexpr int PER_LANE = Cfg::FM * Cfg::FN * 4;
+        if (kg > 0) {
+#pragma unroll
+            for (int i = 0; i < Cfg::FM; ++i)
+#pragma unroll
+                for (int j = 0; j < Cfg::FN; ++j)
+                    *(f32x4 LDS*)(red + (((kg - 1) * Cfg::NT + wave * 64 + lane) * PER_LANE +
+                                         (i * Cfg::FN + j) * 4)) = acc[i][j];
+        }
+        lds_barrier();
+        if (kg != 0)
+            return;
+#pragma unroll
+        for (int c = 1; c < KG; ++c)
+#pragma unroll
+            for (int i = 0; i < Cfg::FM; ++i)
+#pragma unroll
+                for (int j = 0; j < Cfg::FN; ++j)
+                    acc[i][j] += *(const f32x4 LDS*)(red + (((c - 1) * Cfg::NT + wave * 64 + lane) *
+                                                                PER_LANE +
+                                                            (i * Cfg::FN + j) * 4));
+    }
     // lane holds C[16i + 4g + r][16j + q] of the wave tile
     const float gab = *gA * *gB;
 #pragma unroll
@@ -356,30 +393,58 @@ __global__ __launch_bounds__(Cfg::NT) void gemm_nvfp4_kernel(
         }
 }
 
-template <class Cfg>
+template <class Cfg, int KG = 1>
 static hipError_t launch_nvfp4_cfg(const void* A_q, const uint8_t* sA, const float* gA,
                                    const void* B_q, const uint8_t* sB, const float* gB, void* C,
                                    int64_t M, int64_t N, int64_t K, int out_bf16,
                                    hipStream_t stream)
 {
     const int64_t tiles = ((M + Cfg::BM - 1) / Cfg::BM) * (N / Cfg::BN);
-    if (!grid_fits(tiles, Cfg::NT))
+    if (!grid_fits(tiles, Cfg::NT * KG))
         return hipErrorInvalidConfiguration;
     if (out_bf16)
-        hipLaunchKernelGGL((gemm_nvfp4_kernel<Cfg, true>), dim3((unsigned)tiles), dim3(Cfg::NT),
-                           0, stream, static_cast<const uint8_t*>(A_q), sA, gA,
-                           static_cast<const uint8_t*>(B_q), sB, gB, C, M, N, K);
+        hipLaunchKernelGGL((gemm_nvfp4_kernel<Cfg, true, KG>), dim3((unsigned)tiles),
+                           dim3(Cfg::NT * KG), 0, stream, static_cast<const uint8_t*>(A_q), sA,
+                           gA, static_cast<const uint8_t*>(B_q), sB, gB, C, M, N, K);
     else
-        hipLaunchKernelGGL((gemm_nvfp4_kernel<Cfg, false>), dim3((unsigned)tiles), dim3(Cfg::NT),
-                           0, stream, static_cast<const uint8_t*>(A_q), sA, gA,
-                           static_cast<const uint8_t*>(B_q), sB, gB, C, M, N, K);
+        hipLaunchKernelGGL((gemm_nvfp4_kernel<Cfg, false, KG>), dim3((unsigned)tiles),
+                           dim3(Cfg::NT * KG), 0, stream, static_cast<const uint8_t*>(A_q), sA,
+                           gA, static_cast<const uint8_t*>(B_q), sB, gB, C, M, N, K);
     return hipGetLastError();
 }
+
+// few output tiles: 64x32 tiles (2 waves of 32x32) with the K chunks over 4 wave groups while
+// they fit one round of the CUs, else 64x64 tiles (4 waves of 32x32) over 2 wave groups
+#ifndef FGQ_NVFP4_NARROW_CFG
+#define FGQ_NVFP4_NARROW_CFG 64, 32, 2, 1
+#endif
+#ifndef FGQ_NVFP4_NARROW_KG
+#define FGQ_NVFP4_NARROW_KG 4
+#endif
+#ifndef FGQ_NVFP4_SMALL_CFG
+#define FGQ_NVFP4_SMALL_CFG 64, 64, 2, 2
+#endif
+#ifndef FGQ_NVFP4_SMALL_KG
+#define FGQ_NVFP4_SMALL_KG 2
+#endif
 
 hipError_t launch_gemm_nvfp4(const void* A_q, const uint8_t* sA, const float* gA,
                              const void* B_q, const uint8_t* sB, const float* gB, void* C,
                              int64_t M, int64_t N, int64_t K, int out_bf16, hipStream_t stream)
 {
+    // 128x128 tiles while they cover the 256 CUs at least once (256x128 from M = 256); fewer
+    // tiles than that: the K-split families above (measured back to back: 128x7168x2048 21.7 ->
+    // 10.6 us, 1x7168x2048 20.3 -> 7.0 us, 128x256x512 7.9 -> 4.5 us)
+    const int64_t tiles128 = ((M + 127) / 128) * (N / 128);
+    if (tiles128 < 256) {
+        using Narrow = Nvfp4Cfg<FGQ_NVFP4_NARROW_CFG>;
+        const int cus = device_cus() > 0 ? device_cus() : 256;
+        if (((M + Narrow::BM - 1) / Narrow::BM) * (N / Narrow::BN) <= cus)
+            return launch_nvfp4_cfg<Narrow, FGQ_NVFP4_NARROW_KG>(A_q, sA, gA, B_q, sB, gB, C, M,
+                                                                 N, K, out_bf16, stream);
+        return launch_nvfp4_cfg<Nvfp4Cfg<FGQ_NVFP4_SMALL_CFG>, FGQ_NVFP4_SMALL_KG>(
+            A_q, sA, gA, B_q, sB, gB, C, M, N, K, out_bf16, stream);
+    }
     if (M >= 256)
         return launch_nvfp4_cfg<Nvfp4Cfg<256, 128, 4, 2>>(A_q, sA, gA, B_q, sB, gB, C, M, N, K,
                                                           out_bf16, stream);

@@ -103,8 +103,13 @@ def random_nvfp4(rows, K, rng):
 
 
 @pytest.mark.parametrize("M,N,K", [
+    # few output tiles: the 64x32 K-split family ...
     (1, 128, 128), (7, 128, 384), (129, 256, 256), (300, 512, 640), (512, 256, 128),
     (64, 1024, 1152), (33, 128, 0),
+    # ... the 64x64 K-split family (too many 64x32 tiles for one round), odd chunk counts
+    (129, 7168, 384), (200, 8192, 256),
+    # the wide families, ragged M
+    (300, 32768, 128), (130, 32768, 256),
 ])
 @pytest.mark.parametrize("out", ["f32", "bf16"])
 def test_gemm_edge_shapes(M, N, K, out):
