@@ -131,8 +131,11 @@ int fgq_gemm_fp8_blockscaled_variant(const void* A_q, const float* scale_A, cons
  *   C_q     out: E4M3FN [M, N]         } exactly fgq_quantize_act_1x128 applied to the C
  *   scale_C out: fp32 [M, N/128]        } written here (bit for bit)
  * Arguments, requirements and errors as fgq_gemm_fp8_blockscaled; none of the three outputs
- * may overlap each other or an input.  Always runs the wide kernel family (each workgroup
- * owns whole 128-column groups of its rows).
+ * may overlap each other or an input.  One launch of the wide kernel family (each workgroup
+ * owns whole 128-column groups of its rows) when its 128x128 tiles cover the GPU's CUs at
+ * least once; for shapes with fewer tiles, where those tiles would leave CUs idle, the call
+ * enqueues the GEMM family fgq_gemm_fp8_blockscaled would pick and then the activation
+ * quantizer over that C (two launches on the stream, same contract).
  */
 int fgq_gemm_fp8_blockscaled_quant(const void* A_q, const float* scale_A, const void* B_q,
                                    const float* scale_B, void* C, void* C_q, float* scale_C,

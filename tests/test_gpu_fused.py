@@ -30,7 +30,11 @@ def gpu_fused(Aq, sA, Bq, sB):
 
 
 def family(M, N):
-    """the wide kernel family the fused call runs for this shape (1: 256x128, 2: 128x128)"""
+    """the GEMM the fused call runs for this shape: the fused wide kernel (1: 256x128,
+    2: 128x128) when its 128x128 tiles cover the 256 CUs, else the automatic choice (0) of
+    the plain GEMM followed by the quantizer"""
+    if ((M + 127) // 128) * (N // 128) < 256:
+        return 0
     return 1 if M >= 256 and ((M + 255) // 256) * (N // 128) >= 256 else 2
 
 
@@ -41,8 +45,11 @@ def check_quant_of_c(bits, Cq, sC):
 
 
 @pytest.mark.parametrize("M,N,K", [
+    # few output tiles: the GEMM family of the shape, then the quantizer
     (1, 128, 128), (7, 128, 384), (129, 256, 256), (255, 384, 128), (300, 512, 640),
     (512, 512, 384), (64, 1024, 1152), (33, 128, 0),
+    # the fused kernel (256x128 and 128x128 tiles), ragged M
+    (300, 16384, 256), (129, 32768, 128),
 ])
 def test_fused_edge_shapes(M, N, K):
     log(f"fused edge M={M} N={N} K={K}")
