@@ -204,3 +204,26 @@ def test_coder_division_is_correctly_rounded(markstein_lib):
                                         ctypes.byref(sign_err), ctypes.byref(checked))
     assert checked.value > 5_000_000
     assert bad == 0 and code_err.value == 0 and sign_err.value == 0
+
+
+def test_block_and_tensor_amax_at_every_position():
+    """A block's E4M3 scale follows its largest magnitude at each of the block's 16 positions,
+    and the global scale follows the tensor's largest magnitude when it is the very last
+    element: g = fl32(6/2688), every block whose maximum is 3 gets ENC(fl32(3/fl32(6g)))."""
+    rng = np.random.default_rng(5)
+    R = 16
+    small = rng.integers(0x3A00, 0x3EFF, (R, 32)).astype(np.uint16)   # |x| < 0.5
+    small |= (rng.integers(0, 2, (R, 32)) << 15).astype(np.uint16)
+    X = small
+    for r in range(R):
+        X[r, r] = 0x4040                   # 3.0 at position r of block 0
+        X[r, 16 + (15 - r)] = 0xC040       # -3.0 at position 15 - r of block 1
+    X[R - 1, 31] = 0x40C0                  # 6.0, the tensor's maximum, last element
+    Xq, sX, g = oracle.quantize_nvfp4(X)
+    g_want = np.float32(6.0) / np.float32(2688.0)
+    assert g == g_want
+    six_g = np.float32(6.0) * g_want
+    s3 = oracle.e4m3_encode(np.array([np.float32(3.0) / six_g], dtype=np.float32))[0]
+    s6 = oracle.e4m3_encode(np.array([np.float32(6.0) / six_g], dtype=np.float32))[0]
+    assert np.all(sX[:, 0] == s3)
+    assert np.all(sX[:R - 1, 1] == s3) and sX[R - 1, 1] == s6

@@ -183,3 +183,57 @@ def test_domain_sweep_properties():
     vpos = oracle.e4m3_decode(fq[pos])
     same = np.diff(fa[pos]) == 0
     assert np.all(np.diff(vpos)[same] >= 0)
+
+
+# (amax, x) bf16 pairs where a reciprocal multiply x * fl32(1/s) and the correctly rounded
+# divide fl32(x / s) give different E4M3 codes (found by search over bf16 pairs)
+DIVIDE_CASES = [(16810, 14762), (16978, 14870), (16978, 15043), (16376, 14522),
+                (16376, 14650), (17094, 15046)]
+
+
+def test_divide_not_reciprocal_cases(helper_lib):
+    """Codes come from the correctly rounded quotient x/s: on the pairs where x*(1/s) rounds to
+    another code, the oracle agrees with the exact-rational brute force."""
+    X = np.zeros((len(DIVIDE_CASES), 128), dtype=np.uint16)
+    for r, (a, x) in enumerate(DIVIDE_CASES):
+        X[r, 0], X[r, 77] = a, x
+    Xq, sX = oracle.quantize_act(X)
+    for r in range(len(DIVIDE_CASES)):
+        codes, s = _expected_codes_exact(X[r], helper_lib)
+        assert np.float32(sX[r, 0]) == np.float32(s)
+        assert Xq[r, 77] == codes[77], r
+
+
+def _one_max_rows(n, rng):
+    """n rows of 128 small bf16 values (|x| < 1) whose unique largest magnitude, 3.5 with
+    alternating sign, sits at column r of row r"""
+    X = (np.abs(_rand_bf16((n, 128), rng, 0.2)) & 0x7FFF) | (rng.integers(0, 2, (n, 128)) << 15)
+    X = X.astype(np.uint16)
+    X[(X & 0x7FFF) >= 0x3F80] &= 0x803F          # keep |x| < 1
+    for r in range(n):
+        X[r, r % 128] = 0x4060 | ((r & 1) << 15)  # +-3.5
+    return X
+
+
+def test_amax_at_every_position():
+    """The scale follows a group's largest magnitude wherever it sits: a 1x128 tile with it at
+    each of the 128 positions, a 128x128 block with it at corners, edges and inside, for the
+    fp32 and UE8M0 scales -- s = fl32(3.5/448), e = 120 (448 * 2^-7 is the first power-of-two
+    multiple of 448 that covers 3.5) -- and its own code is the saturating +-448."""
+    rng = np.random.default_rng(3)
+    X = _one_max_rows(128, rng)
+    s_want = np.float32(3.5) / np.float32(448.0)
+    Xq, sX = oracle.quantize_act(X)
+    assert np.all(sX[:, 0] == s_want)
+    for r in range(128):
+        assert Xq[r, r] == (0x7E | ((r & 1) << 7)), r
+    Xq, eX = oracle.quantize_act_ue8m0(X)
+    assert np.all(eX[:, 0] == 120)
+    for (i, j) in [(0, 0), (0, 127), (127, 0), (127, 127), (64, 63), (1, 126)]:
+        W = _one_max_rows(128, rng)
+        W[np.arange(128), np.arange(128)] = 0x3E00    # 0.125: no longer the maximum
+        W[i, j] = 0xC060                              # -3.5
+        Wq, sW = oracle.quantize_weight(W)
+        assert sW[0, 0] == s_want and Wq[i, j] == 0xFE, (i, j)
+        _, eW = oracle.quantize_weight_ue8m0(W)
+        assert eW[0, 0] == 120, (i, j)
