@@ -62,6 +62,16 @@ MUTANTS = {
         "for (int j = 0; j < 15; ++j) {\n                float v = fabsf("),
     "NVFP4 tensor amax misses the last element": (
         "for (int64_t i = 0; i < R * C; ++i) {", "for (int64_t i = 0; i + 1 < R * C; ++i) {"),
+    "GEMM tolerance sum of signed products": (
+        "srow[n] += fabs(p);", "srow[n] += p;"),
+    "UE8M0 decode bias 126": (
+        "return ldexp(1.0, (int)e - 127);", "return ldexp(1.0, (int)e - 126);"),
+    "NVFP4 GEMM nibble order swapped for B": (
+        "uint8_t code = (k % 2 == 0) ? (byte & 15) : (byte >> 4);\n                double b",
+        "uint8_t code = (k % 2 == 1) ? (byte & 15) : (byte >> 4);\n                double b"),
+    "NVFP4 GEMM block scale of A one block late": (
+        "oracle_e4m3_decode(sA[m * KB + k / 16])",
+        "oracle_e4m3_decode(sA[m * KB + (k / 16 + 1) % KB])"),
 }
 
 
