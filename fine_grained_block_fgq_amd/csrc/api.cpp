@@ -34,7 +34,8 @@ int check_act(const void* X, const void* Xq, const void* sX, int64_t M, int64_t 
 {
     if (M < 0 || K < 0 || K % 128 != 0 || M > kMaxDim || K > kMaxDim)
         return FGQ_ERR_SHAPE;
-    if (M > 0 && K > 0 && M > ((int64_t(1) << 38) / K))
+    // one launch: M*K/16 work-items, counted in 32 bits
+    if (M > 0 && K > 0 && M > ((int64_t(1) << 36) / K))
         return FGQ_ERR_SHAPE;
     if (M == 0 || K == 0)
         return FGQ_OK;
@@ -228,7 +229,8 @@ int fgq_quantize_nvfp4(const void* X, void* Xq, uint8_t* scale_X, float* global_
 {
     if (R < 0 || C < 0 || C % 16 != 0 || R > kMaxDim || C > kMaxDim)
         return FGQ_ERR_SHAPE;
-    if (R > 0 && C > 0 && R > ((int64_t(1) << 38) / C))
+    // one coding launch: R*C/8 work-items, counted in 32 bits
+    if (R > 0 && C > 0 && R > ((int64_t(1) << 35) / C))
         return FGQ_ERR_SHAPE;
     if (R == 0 || C == 0)
         return FGQ_OK;

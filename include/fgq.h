@@ -57,7 +57,7 @@ typedef enum { FGQ_OUT_F32 = 0, FGQ_OUT_BF16 = 1 } fgq_out_dtype;
  *   Xq      out: E4M3FN codes [M, K] row-major (M*K bytes)
  *   scale_X out: fp32 [M, K/128] row-major; scale_X[m*(K/128)+kb] = amax/448 of
  *                X[m, 128kb .. 128kb+127]
- * Requires M >= 0, K >= 0, K % 128 == 0, M*K <= 2^38.
+ * Requires M >= 0, K >= 0, K % 128 == 0, M*K <= 2^36 (the elements one launch covers).
  */
 int fgq_quantize_act_1x128(const void* X, void* Xq, float* scale_X, int64_t M, int64_t K,
                            void* stream);
@@ -172,7 +172,7 @@ int fgq_gemm_fp8_blockscaled_ue8m0(const void* A_q, const uint8_t* scale_A, cons
  * tensor; value = global * block * e2m1.  Scales: global = amax/2688 (2688 = 448*6),
  * block = E4M3(amax_block / (6*global)), code = E2M1(x / (block*global)) nearest-even,
  * saturating at 6 (signed zeros where block*global is 0).
- *   X            in : bf16 [R, C] row-major, C % 16 == 0, R*C <= 2^38
+ *   X            in : bf16 [R, C] row-major, C % 16 == 0, R*C <= 2^35
  *   Xq           out: packed codes [R, C/2], element 2i in the low nibble of byte i
  *   scale_X      out: E4M3 [R, C/16]
  *   global_scale out: one fp32 (also used as scratch by the call until it completes)
