@@ -192,3 +192,37 @@ def test_grid_limit_is_a_shape_error():
     # skinny GEMM: 2^23 tiles of 768 threads
     assert lib.fgq_gemm_fp8_blockscaled_variant(P, 0x40000, T40, 0x100000, T42, 128, 1 << 28,
                                                 128, 0, 4, None) == -2
+
+
+# The binding has no CPU path: every entry point refuses host tensors before calling the
+# library (which would otherwise dereference host pointers as device addresses).
+def _host(shape, dtype):
+    import torch
+    return torch.zeros(shape, dtype=dtype)
+
+
+def test_binding_refuses_host_tensors():
+    import torch
+    bf, u8, f32 = torch.bfloat16, torch.uint8, torch.float32
+    calls = [
+        lambda: fgq.fgq_quantize_act_1x128(_host((4, 128), bf)),
+        lambda: fgq.fgq_quantize_weight_128x128(_host((128, 128), bf)),
+        lambda: fgq.fgq_quantize_act_1x128_ue8m0(_host((4, 128), bf)),
+        lambda: fgq.fgq_quantize_weight_128x128_ue8m0(_host((128, 128), bf)),
+        lambda: fgq.fgq_quantize_nvfp4(_host((4, 32), bf)),
+        lambda: fgq.fgq_gemm_fp8_blockscaled(_host((4, 128), u8), _host((4, 1), f32),
+                                             _host((128, 128), u8), _host((1, 1), f32)),
+        lambda: fgq.fgq_gemm_fp8_blockscaled_variant(_host((4, 128), u8), _host((4, 1), f32),
+                                                     _host((128, 128), u8), _host((1, 1), f32),
+                                                     variant=3),
+        lambda: fgq.fgq_gemm_fp8_blockscaled_quant(_host((4, 128), u8), _host((4, 1), f32),
+                                                   _host((128, 128), u8), _host((1, 1), f32)),
+        lambda: fgq.fgq_gemm_fp8_blockscaled_ue8m0(_host((4, 128), u8), _host((4, 1), u8),
+                                                   _host((128, 128), u8), _host((1, 1), u8)),
+        lambda: fgq.fgq_gemm_nvfp4(_host((4, 64), u8), _host((4, 8), u8), _host((1,), f32),
+                                   _host((128, 64), u8), _host((128, 8), u8), _host((1,), f32)),
+        lambda: fgq.fgq_probe_fp8_mfma_partials(_host((16, 128), u8), _host((128, 16), u8)),
+    ]
+    for i, call in enumerate(calls):
+        with pytest.raises(TypeError, match="CUDA"):
+            call()
