@@ -69,3 +69,42 @@ def test_random_shape(i, M, N, K, variant, bf16):
     torch.cuda.synchronize()
     Cr4, S4 = oracle.gemm_nvfp4_f64(a4, sa4, gA, b4, sb4, gB)
     assert gemm_error_ratio(C4.cpu().numpy().astype(np.float64), Cr4, S4, False) <= 1.0
+
+
+def quant_shapes():
+    rng = np.random.default_rng(77)
+    return [(i, int(rng.integers(1, 301)), 128 * int(rng.integers(1, 33)),
+             16 * int(rng.integers(1, 257))) for i in range(30)]
+
+
+def bf16_data(rng, shape):
+    """bf16 bits: normals over a wide magnitude range, a few outliers, an all-zero row part"""
+    x = rng.standard_normal(shape) * 10.0 ** rng.uniform(-6, 4, shape[0])[:, None]
+    x[rng.random(shape) < 0.001] *= 300.0
+    h = (x.astype(np.float32).view(np.uint32) >> 16).astype(np.uint16)
+    if shape[1] >= 256:
+        h[0, 128:256] = 0
+    return h
+
+
+@pytest.mark.parametrize("i,M,K,C", quant_shapes())
+def test_random_shape_quantizers(i, M, K, C):
+    from tests.gpu_util import dev_bf16, gpu_quant_act, gpu_quant_weight
+    rng = np.random.default_rng(500 + i)
+    log(f"random quantizer shapes {i}: act/ue8m0 [{M},{K}], weight [{K},{min(K, 1024)}], nvfp4 [{M},{C}]")
+    X = bf16_data(rng, (M, K))
+    q, s = gpu_quant_act(X)
+    rq, rs = oracle.quantize_act(X)
+    assert np.array_equal(q, rq) and np.array_equal(s.view(np.uint32), rs.view(np.uint32))
+    q, e = fgq.fgq_quantize_act_1x128_ue8m0(dev_bf16(X))
+    rq, re = oracle.quantize_act_ue8m0(X)
+    assert np.array_equal(q.cpu().numpy(), rq) and np.array_equal(e.cpu().numpy(), re)
+    W = bf16_data(rng, (K, min(K, 1024)))
+    q, s = gpu_quant_weight(W)
+    rq, rs = oracle.quantize_weight(W)
+    assert np.array_equal(q, rq) and np.array_equal(s.view(np.uint32), rs.view(np.uint32))
+    Y = bf16_data(rng, (M, C))
+    q, s, g = fgq.fgq_quantize_nvfp4(dev_bf16(Y))
+    rq, rs, rg = oracle.quantize_nvfp4(Y)
+    assert np.array_equal(q.cpu().numpy(), rq) and np.array_equal(s.cpu().numpy(), rs)
+    assert np.float32(g.cpu().numpy()[0]).view(np.uint32) == np.float32(rg).view(np.uint32)
