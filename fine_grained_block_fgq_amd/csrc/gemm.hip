@@ -142,6 +142,54 @@ struct ScaleIn<true> {
     }
 };
 
+// The scale_B values one wave uses, one per chunk it computes, taken in order i = 0, 1, ...
+// from p[i * stride] (i < n).  fp32 scales come by scalar loads, each issued one chunk ahead so
+// that it completes under the LDS barrier's wait.  UE8M0 bytes can only come by vector loads,
+// and a chunk waiting for its own byte would also wait for every operand prefetch in flight;
+// so the bytes of 64 chunks are loaded at once, one per lane, and chunk i reads lane i % 64.
+template <class SI>
+struct ScaleBWalk;
+template <>
+struct ScaleBWalk<ScaleIn<false>> {
+    const float* p;
+    int64_t stride, n;
+    float next;
+    __device__ __forceinline__ ScaleBWalk(const float* p_, int64_t stride_, int64_t n_, int)
+        : p(p_), stride(stride_), n(n_), next(n_ > 0 ? p_[0] : 0.0f)
+    {
+    }
+    __device__ __forceinline__ float get(int64_t i)
+    {
+        const float v = next;
+        if (i + 1 < n)
+            next = p[(i + 1) * stride];
+        return v;
+    }
+};
+template <>
+struct ScaleBWalk<ScaleIn<true>> {
+    const uint8_t* p;
+    int64_t stride, n;
+    int lane, raw;
+    __device__ __forceinline__ ScaleBWalk(const uint8_t* p_, int64_t stride_, int64_t n_,
+                                          int lane_)
+        : p(p_), stride(stride_), n(n_), lane(lane_)
+    {
+        fill(0);
+    }
+    __device__ __forceinline__ void fill(int64_t i0)
+    {
+        const int64_t i = i0 + lane;
+        raw = i < n ? (int)p[i * stride] : 127;
+    }
+    __device__ __forceinline__ float get(int64_t i)
+    {
+        if ((i & 63) == 0 && i > 0)
+            fill(i);
+        return ScaleIn<true>::value((uint8_t)__builtin_amdgcn_readlane(raw, (int)(i & 63)));
+    }
+};
+
 
 template <class Cfg, class SI>
 __device__ __forceinline__ void load_stage(uint8_t LDS* stage, const uint8_t* __restrict__ A,
@@ -443,10 +491,8 @@ __global__ __launch_bounds__(Cfg::NT) void gemm_fp8_blockscaled_kernel(
         for (int j = 0; j < Cfg::FN; ++j)
             acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-    // scale_B of the wave's column block, loaded one chunk ahead: the scalar load then
-    // completes under the LDS barrier's wait instead of stalling the chunk's LDS reads
-    const typename SI::T* const sB_col = sB + (nb_wave < NB ? nb_wave : NB - 1);
-    float sb_next = KB > 0 ? SI::value(sB_col[0]) : 0.0f;
+    // scale_B of the wave's column block, chunk by chunk
+    ScaleBWalk<SI> sbw(sB + (nb_wave < NB ? nb_wave : NB - 1), NB, KB, lane);
 
     // prologue: the first STAGES-1 chunks in flight
 #pragma unroll
@@ -467,7 +513,6 @@ __global__ __launch_bounds__(Cfg::NT) void gemm_fp8_blockscaled_kernel(
             wait_vm<0>();
         // all waves: chunk kb visible, and chunk kb-1 fully read (its buffer may refill)
         lds_barrier();
-        const float sb = sb_next;
         const int64_t nxt = kb + Cfg::STAGES - 1;
 #if FGQ_SPREAD_DMA
         // chunk nxt's loads go out a few at a time between this chunk's column blocks
@@ -479,8 +524,7 @@ __global__ __launch_bounds__(Cfg::NT) void gemm_fp8_blockscaled_kernel(
                             nxt, wave, lane);
         const NoLoader loader;
 #endif
-        if (kb + 1 < KB)
-            sb_next = SI::value(sB_col[(kb + 1) * NB]);
+        const float sb = sbw.get(kb);
         compute_chunk<Cfg, SI>(cur, fo, s_off, sb, acc, loader);
         if (Cfg::STAGES == 2)
             lds_barrier();   // keeps the waves in step (measured faster than letting them drift)
@@ -590,6 +634,7 @@ __global__ __launch_bounds__(Cfg::NT * KG) void gemm_fp8_blockscaled_ksplit_kern
             acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
     // this group's chunk of step s is kb = s*KG + kg (if < KB)
+    ScaleBWalk<SI> sbw(sB + kg * NB + nb, KG * NB, kg < KB ? (KB - kg + KG - 1) / KG : 0, lane);
     auto stage_of = [&](int64_t st) { return smem + ((st % Cfg::STAGES) * KG + kg) * Cfg::STAGE; };
 #pragma unroll
     for (int st = 0; st < Cfg::STAGES - 1; ++st)
@@ -615,7 +660,7 @@ __global__ __launch_bounds__(Cfg::NT * KG) void gemm_fp8_blockscaled_ksplit_kern
             load_stage<Cfg, SI>(stage_of(nxt), A, sA, B, M, N, K, m0, n0, nxt * KG + kg, wl,
                                 lane);
         if (kb < KB) {
-            const float sb = SI::value(sB[kb * NB + nb]);
+            const float sb = sbw.get(st);
             compute_chunk<Cfg, SI>(stage_of(st), fo, s_off, sb, acc);
         }
         if (Cfg::STAGES == 2)
@@ -799,6 +844,7 @@ __global__ __launch_bounds__(Cfg::NT) void gemm_fp8_blockscaled_narrow_kernel(
 
     // this wave's chunks: kb = wave + c*KW, c < nc
     const int64_t nc = wave < KB ? (KB - wave + Cfg::KW - 1) / Cfg::KW : 0;
+    ScaleBWalk<SI> sbw(sB + wave * NB + nb, Cfg::KW * NB, nc, lane);
 #pragma unroll
     for (int st = 0; st < Cfg::STAGES - 1; ++st)
         if (st < nc)
@@ -817,8 +863,7 @@ __global__ __launch_bounds__(Cfg::NT) void gemm_fp8_blockscaled_narrow_kernel(
         if (nxt < nc)
             narrow_load<Cfg, SI>(ring + (nxt % Cfg::STAGES) * Cfg::STAGE, A, sA, B, M, N, K, m0,
                              n0, wave + nxt * Cfg::KW, lane);
-        const int64_t kb = wave + c * Cfg::KW;
-        const float sb = SI::value(sB[kb * NB + nb]);
+        const float sb = sbw.get(c);
         compute_chunk<Cfg, SI>(ring + (c % Cfg::STAGES) * Cfg::STAGE, fo, s_off, sb, acc);
     }
 
