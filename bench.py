@@ -264,7 +264,79 @@ def cpu_model():
     return None
 
 
-def cpu_baseline(A, B, step_out=None):
+NVFP4_ORACLE_ROWS = 128   # rows of the 4096^3 NVFP4 GEMM the (slower) NVFP4 oracle computes
+
+
+def tolerance(C_ref, S, bf16):
+    """|C - C_ref| bound of the parity tests: 1e-5*sum|ab| + 1e-6, plus one bf16 ulp of the
+    reference for bf16 output"""
+    tol = 1e-5 * S + 1e-6
+    if bf16:
+        mag = np.maximum(np.abs(C_ref) + tol, 2.0 ** -126)
+        tol = tol + 2.0 ** (np.floor(np.log2(mag)) - 7)
+    return tol
+
+
+def next_rows_baseline(A, B, C_ref, S, nxt, nt):
+    """The oracle on the fused-epilogue, UE8M0 and NVFP4 variants of the 4096^3 step, timed,
+    and the GPU's outputs of each checked against it (codes and scales bit for bit, GEMM
+    outputs as a fraction of the tolerance)."""
+    import oracle
+    out = {}
+    bits, Cq, sC = nxt["fused"]
+    t0 = time.perf_counter()
+    rq, rs = oracle.quantize_act(bits, nt)
+    t1 = time.perf_counter()
+    C = (bits.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    out["fused_epilogue"] = {
+        "sample": "oracle 1x128 quantization of the fused call's own bf16 C (all 4096 rows); "
+                  "C against the fp64 GEMM of the main leg",
+        "quantize_seconds": round(t1 - t0, 3),
+        "codes_bit_exact": bool(np.array_equal(Cq, rq)),
+        "scales_bit_exact": bool(np.array_equal(sC.view(np.uint32), rs.view(np.uint32))),
+        "gemm_max_error_over_tolerance": float(np.max(np.abs(C - C_ref) / tolerance(C_ref, S, True))),
+    }
+    gAq, geA, gBq, geB, gC = nxt["ue8m0"]
+    M, K = A.shape
+    N = B.shape[1]
+    t0 = time.perf_counter()
+    Aq, eA = oracle.quantize_act_ue8m0(A, nt)
+    Bq, eB = oracle.quantize_weight_ue8m0(B, nt)
+    t1 = time.perf_counter()
+    Cu, Su = oracle.gemm_f64(Aq, oracle.ue8m0_decode(eA), Bq, oracle.ue8m0_decode(eB), nt)
+    t2 = time.perf_counter()
+    out["ue8m0"] = {
+        "value": 2.0 * M * N * K / (t2 - t1) / 1e12, "unit": "TFLOP/s",
+        "sample": f"whole 4096^3 step: UE8M0 quantize A and B ({t1 - t0:.2f} s), fp64 GEMM of "
+                  f"all rows ({t2 - t1:.2f} s)",
+        "codes_bit_exact": bool(np.array_equal(gAq, Aq) and np.array_equal(gBq, Bq)),
+        "scales_bit_exact": bool(np.array_equal(geA, eA) and np.array_equal(geB, eB)),
+        "gemm_max_error_over_tolerance": float(np.max(np.abs(gC - Cu) / tolerance(Cu, Su, True))),
+    }
+    del Cu, Su
+    gA4, gsA4, ggA, gB4, gsB4, ggB, gC4 = nxt["nvfp4"]
+    rows = gC4.shape[0]
+    t0 = time.perf_counter()
+    A4, sA4, gA = oracle.quantize_nvfp4(A)
+    B4, sB4, gB = oracle.quantize_nvfp4(np.ascontiguousarray(B.T))
+    t1 = time.perf_counter()
+    C4, S4 = oracle.gemm_nvfp4_f64(A4, sA4, gA, B4, sB4, gB, nt, rows=(0, rows))
+    t2 = time.perf_counter()
+    C4, S4 = C4[:rows], S4[:rows]
+    out["nvfp4"] = {
+        "value": 2.0 * rows * N * K / (t2 - t1) / 1e12, "unit": "TFLOP/s",
+        "sample": f"NVFP4 quantize of A and B^T [4096,4096] ({t1 - t0:.2f} s, one thread), fp64 "
+                  f"GEMM of the first {rows} rows ({t2 - t1:.2f} s)",
+        "codes_bit_exact": bool(np.array_equal(gA4, A4) and np.array_equal(gB4, B4)),
+        "scales_bit_exact": bool(np.array_equal(gsA4, sA4) and np.array_equal(gsB4, sB4)
+                                 and ggA.view(np.uint32)[0] == np.float32(gA).view(np.uint32)
+                                 and ggB.view(np.uint32)[0] == np.float32(gB).view(np.uint32)),
+        "gemm_max_error_over_tolerance": float(np.max(np.abs(gC4 - C4) / tolerance(C4, S4, True))),
+    }
+    return out
+
+
+def cpu_baseline(A, B, step_out=None, next_out=None):
     """The oracle as it stands (scalar C, all host threads over independent rows) on the
     4096^3 workload: quantize A and B, then the fp64 GEMM for all rows.  With the GPU step's
     own outputs (codes, scales, bf16 C, computed on the GPU from the same bf16 inputs), the
@@ -284,15 +356,14 @@ def cpu_baseline(A, B, step_out=None):
     parity = None
     if step_out is not None:
         gAq, gsA, gBq, gsB, gC = step_out
-        tol = 1e-5 * S + 1e-6
-        mag = np.maximum(np.abs(C_ref) + tol, 2.0 ** -126)
-        tol = tol + 2.0 ** (np.floor(np.log2(mag)) - 7)          # one bf16 ulp
+        tol = tolerance(C_ref, S, True)
         parity = {
             "codes_bit_exact": bool(np.array_equal(gAq, Aq) and np.array_equal(gBq, Bq)),
             "scales_bit_exact": bool(np.array_equal(gsA.view(np.uint32), sA.view(np.uint32))
                                      and np.array_equal(gsB.view(np.uint32), sB.view(np.uint32))),
             "gemm_max_error_over_tolerance": float(np.max(np.abs(gC - C_ref) / tol)),
         }
+    nxt = None if next_out is None else next_rows_baseline(A, B, C_ref, S, next_out, nt)
     return {
         "value": 2.0 * M * N * K / (t2 - t1) / 1e12,
         "unit": "TFLOP/s",
@@ -305,7 +376,43 @@ def cpu_baseline(A, B, step_out=None):
         "seconds": t2 - t0,
         "cpu_model": cpu_model(),
         "parity_of_the_gpu_step": parity,
+        "next_rows": nxt,
     }
+
+
+def step_outputs(torch, fgq, A, B, dev):
+    """The outputs of one more pass of each timed 4096^3 step, on the same resident inputs, for
+    the oracle comparison: the FP8 step (codes, scales, bf16 C), the fused GEMM + quantization
+    of C, the UE8M0 step and the NVFP4 step (C of its first rows only).  Taken after every
+    timed region, so that the host copies do not leave the GPU idle (and its clock lowered)
+    before a measurement."""
+    M, K = A.shape
+    N = B.shape[1]
+
+    def host(t):
+        return t.cpu().numpy()
+
+    def host_f64(t):
+        return t.float().cpu().numpy().astype(np.float64)
+
+    Aq, sA = fgq.fgq_quantize_act_1x128(A)
+    Bq, sB = fgq.fgq_quantize_weight_128x128(B)
+    C = fgq.fgq_gemm_fp8_blockscaled(Aq, sA, Bq, sB)
+    step_out = [host(Aq), host(sA), host(Bq), host(sB), host_f64(C)]
+    Cq = torch.empty((M, N), dtype=torch.uint8, device=dev)
+    sC = torch.empty((M, N // 128), dtype=torch.float32, device=dev)
+    fgq.fgq_gemm_fp8_blockscaled_quant(Aq, sA, Bq, sB, C, Cq, sC)
+    nxt = {"fused": [host(C.view(torch.int16)).view(np.uint16), host(Cq), host(sC)]}
+    qA, eA = fgq.fgq_quantize_act_1x128_ue8m0(A)
+    qB, eB = fgq.fgq_quantize_weight_128x128_ue8m0(B)
+    fgq.fgq_gemm_fp8_blockscaled_ue8m0(qA, eA, qB, eB, C)
+    nxt["ue8m0"] = [host(qA), host(eA), host(qB), host(eB), host_f64(C)]
+    A4, sA4, gA4 = fgq.fgq_quantize_nvfp4(A)
+    B4, sB4, gB4 = fgq.fgq_quantize_nvfp4(B.t().contiguous())
+    fgq.fgq_gemm_nvfp4(A4, sA4, gA4, B4, sB4, gB4, C)
+    nxt["nvfp4"] = [host(A4), host(sA4), host(gA4), host(B4), host(sB4), host(gB4),
+                    host_f64(C[:NVFP4_ORACLE_ROWS])]
+    return step_out, nxt
 
 
 def profile_pass(torch, fgq, synth, dev, reps=3):
@@ -414,10 +521,6 @@ def main():
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     ms_per_step = (t1 - t0) * 1e3 / args.steps
-    # the step's outputs, for the oracle comparison of the cpu_baseline leg
-    step_out = None if args.no_cpu_baseline else [
-        Aq.cpu().numpy(), sA.cpu().numpy(), Bq.cpu().numpy(), sB.cpu().numpy(),
-        C.float().cpu().numpy().astype(np.float64)]
     gm_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in evs]))
     # the two quantizers of the step, each between its own events (outside the timed steps)
     qev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(50)]
@@ -539,6 +642,9 @@ def main():
     log(f"nvfp4: quant A {nv_ms[0]*1e3:.1f} us  quant B {nv_ms[1]*1e3:.1f} us  "
         f"GEMM {nv_ms[2]*1e3:.1f} us")
     del Bt, A4, sA4, gA4, B4, sB4, gB4
+    # algorithmic bytes of one activation quantization in each format
+    ue8_act_bytes = 2 * M * K + M * K + M * (K // 128)
+    nv4_act_bytes = 2 * M * K + M * K // 2 + M * K // 16 + 4
 
     # ---- standalone activation quantizer, X [16384,7168] (rotating buffers) -------------
     wq = synth.WORKLOADS["actq"]
@@ -711,27 +817,38 @@ def main():
             "fused_us": round(fused_ms * 1e3, 2),
             "separate_us": round(sep_ms * 1e3, 2),
             "saved_us": round((sep_ms - fused_ms) * 1e3, 2),
+            "fused_tflops": round(flops / (fused_ms * 1e-3) / 1e12, 1),
+            "fused_frac_fp8_peak": round(flops / (fused_ms * 1e-3) / 1e12 / PEAK_FP8_TFLOPS, 4),
         },
         "ue8m0": {
             "workload": "the 4096^3 step on UE8M0 exponent-byte scales",
             "quantize_act_us": round(ue_ms[0] * 1e3, 2),
+            "quantize_act_frac_hbm_peak": round(ue8_act_bytes / (ue_ms[0] * 1e-3) / 1e9
+                                                / PEAK_HBM_GBS, 4),
             "quantize_weight_us": round(ue_ms[1] * 1e3, 2),
             "gemm_us": round(ue_ms[2] * 1e3, 2),
             "gemm_tflops": round(flops / (ue_ms[2] * 1e-3) / 1e12, 1),
+            "gemm_frac_fp8_peak": round(flops / (ue_ms[2] * 1e-3) / 1e12 / PEAK_FP8_TFLOPS, 4),
+            "gemm_frac_f16_peak": round(flops / (ue_ms[2] * 1e-3) / 1e12 / PEAK_F16_TFLOPS, 4),
         },
         "nvfp4": {
             "workload": "the 4096^3 step in NVFP4 (E2M1, per-16 E4M3 + fp32 global scales)",
             "quantize_act_us": round(nv_ms[0] * 1e3, 2),
+            "quantize_act_frac_hbm_peak": round(nv4_act_bytes / (nv_ms[0] * 1e-3) / 1e9
+                                                / PEAK_HBM_GBS, 4),
             "quantize_weight_us": round(nv_ms[1] * 1e3, 2),
             "gemm_us": round(nv_ms[2] * 1e3, 2),
             "gemm_tflops": round(flops / (nv_ms[2] * 1e-3) / 1e12, 1),
+            "gemm_frac_fp8_peak": round(flops / (nv_ms[2] * 1e-3) / 1e12 / PEAK_FP8_TFLOPS, 4),
+            "gemm_frac_f16_peak": round(flops / (nv_ms[2] * 1e-3) / 1e12 / PEAK_F16_TFLOPS, 4),
         },
         "gemm_configs": gemm_cfgs,
         "cpu_baseline": None,
     }
     if not args.no_cpu_baseline:
         log("timing the CPU oracle on the 4096^3 workload")
-        out["cpu_baseline"] = cpu_baseline(A_bits, B_bits, step_out)
+        step_out, next_out = step_outputs(torch, fgq, A, B, dev)
+        out["cpu_baseline"] = cpu_baseline(A_bits, B_bits, step_out, next_out)
     print(json.dumps(out), flush=True)
 
 

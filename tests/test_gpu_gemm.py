@@ -120,3 +120,19 @@ def test_wave_tail_split(out):
     Cr, S = oracle.gemm_f64(Aq, sA, Bq, sB)
     assert gemm_error_ratio(C, Cr, S, out == "bf16") <= 1.0
     free()
+
+
+@pytest.mark.parametrize("variant", VARIANTS)
+def test_long_k(variant):
+    """K = 33,280 (260 chunks): more than 64 chunks per wave (or per K group) in every family,
+    so scale_B is taken well past the first 64 chunks; scales within a factor 10 of each other
+    keep every chunk's share of C above the tolerance"""
+    M, N, K = 70, 256, 128 * 260
+    rng = np.random.default_rng(260 + variant)
+    Aq, _, Bq, _ = random_operands(M, N, K, seed=260)
+    sA = (10.0 ** rng.uniform(-1, 0, (M, K // 128))).astype(np.float32)
+    sB = (10.0 ** rng.uniform(-1, 0, (K // 128, N // 128))).astype(np.float32)
+    log(f"long K {M}x{N}x{K} variant {variant}")
+    C = gpu_gemm(Aq, sA, Bq, sB, torch.float32, variant)
+    Cr, S = oracle.gemm_f64(Aq, sA, Bq, sB)
+    assert gemm_error_ratio(C, Cr, S, False) <= 1.0

@@ -158,3 +158,19 @@ def test_gemm_workloads(name, variant):
     log(f"  max error ratio {r:.3e}")
     assert r <= 1.0
     free()
+
+
+@pytest.mark.parametrize("variant", [0, 1, 2, 3, 4, 5])
+def test_gemm_long_k(variant):
+    """K = 33,280 (260 chunks): more than 64 chunks per wave (or per K group) in every family,
+    so each wave reloads its scale_B exponent bytes past the first 64 chunks; exponents within
+    2^6 of each other keep every chunk's share of C above the tolerance"""
+    M, N, K = 70, 256, 128 * 260
+    Aq, _, Bq, _ = random_e8_operands(M, N, K, seed=260)
+    rng = np.random.default_rng(261 + variant)
+    eA = rng.integers(124, 131, (M, K // 128)).astype(np.uint8)
+    eB = rng.integers(124, 131, (K // 128, N // 128)).astype(np.uint8)
+    log(f"ue8m0 long K {M}x{N}x{K} variant {variant}")
+    C = gpu_gemm_e8(Aq, eA, Bq, eB, torch.float32, variant)
+    Cr, S = oracle.gemm_f64(Aq, oracle.ue8m0_decode(eA), Bq, oracle.ue8m0_decode(eB))
+    assert gemm_error_ratio(C, Cr, S, False) <= 1.0
