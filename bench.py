@@ -380,6 +380,39 @@ def cpu_baseline(A, B, step_out=None, next_out=None):
     }
 
 
+def time_weight_quantizer(torch, fgq, W, Wq, sW, stream, reps):
+    """The 128x128 weight quantizer on a large weight (the prefill workload's W [16384,7168]),
+    rotating over two buffer sets (704 MB, beyond the 256 MB Infinity Cache): per launch
+    between two events, and back to back."""
+    Ws, Wqs, sWs = [W, W.clone()], [Wq, torch.empty_like(Wq)], [sW, torch.empty_like(sW)]
+    for r in range(16):
+        fgq.fgq_quantize_weight_128x128(Ws[r % 2], Wqs[r % 2], sWs[r % 2], stream)
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(reps)]
+    for r, (a, b) in enumerate(ev):
+        a.record(stream)
+        fgq.fgq_quantize_weight_128x128(Ws[r % 2], Wqs[r % 2], sWs[r % 2], stream)
+        b.record(stream)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for r in range(8):
+        fgq.fgq_quantize_weight_128x128(Ws[r % 2], Wqs[r % 2], sWs[r % 2], stream)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    K, N = W.shape
+    byt = quant_weight_bytes(K, N)
+    us = float(np.mean([a.elapsed_time(b) for a, b in ev])) * 1e3
+    gbs = byt / (us * 1e-6) / 1e9
+    bgbs = byt / (e0.elapsed_time(e1) / 8 * 1e-3) / 1e9
+    log(f"weight quant [{K},{N}]: {us:.1f} us = {gbs:.0f} GB/s per launch, {bgbs:.0f} GB/s "
+        f"back to back")
+    return {"workload": f"weight quantize W [{K},{N}] bf16 -> E4M3 + fp32 [{K // 128},{N // 128}]",
+            "bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+            "frac": round(gbs / PEAK_HBM_GBS, 4), "us": round(us, 2),
+            "back_to_back_GBps": round(bgbs, 1), "back_to_back_frac": round(bgbs / PEAK_HBM_GBS, 4),
+            "algorithmic_bytes": byt}
+
+
 def step_outputs(torch, fgq, A, B, dev):
     """The outputs of one more pass of each timed 4096^3 step, on the same resident inputs, for
     the oracle comparison: the FP8 step (codes, scales, bf16 C), the fused GEMM + quantization
@@ -710,6 +743,8 @@ def main():
         Ac, Bc = to_dev_bf16(Ab, torch), to_dev_bf16(Bb, torch)
         Acq, sAc = fgq.fgq_quantize_act_1x128(Ac, stream=stream)
         Bcq, sBc = fgq.fgq_quantize_weight_128x128(Bc, stream=stream)
+        if name == "prefill":
+            wq_stats = time_weight_quantizer(torch, fgq, Bc, Bcq, sBc, stream, args.quant_reps)
         del Ac, Bc
         out_dt = torch.bfloat16 if wc.out_dtype == "bf16" else torch.float32
         Cc = torch.empty((Mc, Nc), dtype=out_dt, device=dev)
@@ -812,6 +847,7 @@ def main():
             "algorithmic_bytes": q_bytes,
             "traffic": profiled_traffic("quant_act_1x128 16384x7168", "quant_act"),
         },
+        "quantize_weight": wq_stats,
         "fused_epilogue": {
             "workload": "4096^3 GEMM + 1x128 E4M3 quantization of its bf16 C",
             "fused_us": round(fused_ms * 1e3, 2),
