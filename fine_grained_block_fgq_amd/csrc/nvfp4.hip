@@ -16,9 +16,9 @@ namespace fgq {
 
 // ---------------------------------------------------------------------------------------
 // Quantizer.  The global scale needs the tensor amax before any block can be coded, so a
-// call is four launches on one stream: clear the amax slot, reduce |x| into it (integer max
-// of bf16 magnitude bits, order-independent), code every block, then turn the slot into g.
-// The slot is the caller's global-scale output, used as a uint32 until the last launch.
+// call is three launches on one stream: clear the caller's global-scale output, reduce into
+// it (each workgroup's fl32(amax/2688) by an integer max of its bits, order-independent), then
+// code every block with the g it now holds.
 // ---------------------------------------------------------------------------------------
 __global__ void nvfp4_clear_kernel(uint32_t* slot)
 {
@@ -32,14 +32,16 @@ __global__ void nvfp4_clear_kernel(uint32_t* slot)
 // workgroups, each lane taking at least 16 vectors.
 constexpr int NVFP4_AMAX_BLOCKS = 256;
 constexpr int NVFP4_AMAX_VPT = 16;
+constexpr int NVFP4_AMAX_THREADS = 512;   // 8 waves: more loads in flight per CU than 4
+constexpr int NVFP4_AMAX_WAVES = NVFP4_AMAX_THREADS / 64;
 
-__global__ __launch_bounds__(256) void nvfp4_amax_kernel(const u32x4* __restrict__ X,
-                                                         int64_t nvec, uint32_t* slot)
+__global__ __launch_bounds__(NVFP4_AMAX_THREADS) void nvfp4_amax_kernel(
+    const u32x4* __restrict__ X, int64_t nvec, uint32_t* slot)
 {
-    __shared__ uint32_t wave_amax[4];
+    __shared__ uint32_t wave_amax[NVFP4_AMAX_WAVES];
     uint32_t m = 0;
-    const int64_t stride = (int64_t)gridDim.x * 256;
-    int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    const int64_t stride = (int64_t)gridDim.x * NVFP4_AMAX_THREADS;
+    int64_t i = (int64_t)blockIdx.x * NVFP4_AMAX_THREADS + threadIdx.x;
     for (; i + 3 * stride < nvec; i += 4 * stride) {
         const u32x4 a = __builtin_nontemporal_load(&X[i]);
         const u32x4 b = __builtin_nontemporal_load(&X[i + stride]);
@@ -54,8 +56,16 @@ __global__ __launch_bounds__(256) void nvfp4_amax_kernel(const u32x4* __restrict
     if ((threadIdx.x & 63) == 0)
         wave_amax[threadIdx.x >> 6] = m;
     __syncthreads();
-    if (threadIdx.x == 0)
-        atomicMax(slot, max(max(wave_amax[0], wave_amax[1]), max(wave_amax[2], wave_amax[3])));
+    if (threadIdx.x == 0) {
+        uint32_t b = 0;
+#pragma unroll
+        for (int w = 0; w < NVFP4_AMAX_WAVES; ++w)
+            b = max(b, wave_amax[w]);
+        // this workgroup's candidate global scale fl32(amax/2688): a correctly rounded divide
+        // is monotonic, so the largest candidate is the global scale of the tensor amax, and
+        // non-negative fp32 values order like their bit patterns
+        atomicMax(slot, __float_as_uint(__uint_as_float(b << 16) / 2688.0f));
+    }
 }
 
 // E2M1 code of y: count the rounding boundaries passed (ties at 0.25, 1.25, 2.5, 5 go down
@@ -77,8 +87,7 @@ __global__ __launch_bounds__(256) void nvfp4_quant_kernel(const u32x4* __restric
                                                           const uint32_t* __restrict__ slot,
                                                           int64_t nvec)
 {
-    const float amax_t = __uint_as_float(*slot << 16);
-    const float g = amax_t / 2688.0f;
+    const float g = __uint_as_float(*slot);
     const float six_g = 6.0f * g;
     const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
     const u32x4 v = i < nvec ? __builtin_nontemporal_load(&X[i]) : u32x4{0u, 0u, 0u, 0u};
@@ -129,14 +138,6 @@ __global__ __launch_bounds__(256) void nvfp4_quant_kernel(const u32x4* __restric
     }
 }
 
-__global__ void nvfp4_final_kernel(uint32_t* slot)
-{
-    if (threadIdx.x == 0) {
-        const float amax_t = __uint_as_float(*slot << 16);
-        *reinterpret_cast<float*>(slot) = amax_t / 2688.0f;
-    }
-}
-
 hipError_t launch_quant_nvfp4(const void* X, void* Xq, uint8_t* sX, float* g, int64_t R,
                               int64_t C, hipStream_t stream)
 {
@@ -145,14 +146,15 @@ hipError_t launch_quant_nvfp4(const void* X, void* Xq, uint8_t* sX, float* g, in
     if (!grid_fits((nvec + 255) / 256, 256))
         return hipErrorInvalidConfiguration;
     hipLaunchKernelGGL(nvfp4_clear_kernel, dim3(1), dim3(64), 0, stream, slot);
-    int64_t ablocks = (nvec + 256 * NVFP4_AMAX_VPT - 1) / (256 * NVFP4_AMAX_VPT);
+    int64_t ablocks = (nvec + NVFP4_AMAX_THREADS * NVFP4_AMAX_VPT - 1) /
+                      (NVFP4_AMAX_THREADS * NVFP4_AMAX_VPT);
     ablocks = ablocks < 1 ? 1 : (ablocks > NVFP4_AMAX_BLOCKS ? NVFP4_AMAX_BLOCKS : ablocks);
-    hipLaunchKernelGGL(nvfp4_amax_kernel, dim3((unsigned)ablocks), dim3(256), 0, stream,
+    hipLaunchKernelGGL(nvfp4_amax_kernel, dim3((unsigned)ablocks), dim3(NVFP4_AMAX_THREADS), 0,
+                       stream,
                        static_cast<const u32x4*>(X), nvec, slot);
     hipLaunchKernelGGL(nvfp4_quant_kernel, dim3((unsigned)((nvec + 255) / 256)), dim3(256), 0,
                        stream, static_cast<const u32x4*>(X), static_cast<uint32_t*>(Xq), sX,
                        slot, nvec);
-    hipLaunchKernelGGL(nvfp4_final_kernel, dim3(1), dim3(64), 0, stream, slot);
     return hipGetLastError();
 }
 

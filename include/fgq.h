@@ -176,7 +176,7 @@ int fgq_gemm_fp8_blockscaled_ue8m0(const void* A_q, const uint8_t* scale_A, cons
  *   Xq           out: packed codes [R, C/2], element 2i in the low nibble of byte i
  *   scale_X      out: E4M3 [R, C/16]
  *   global_scale out: one fp32 (also used as scratch by the call until it completes)
- * Four launches on `stream` (the tensor amax is needed before any block is coded).
+ * Three launches on `stream` (the tensor amax is needed before any block is coded).
  */
 int fgq_quantize_nvfp4(const void* X, void* Xq, uint8_t* scale_X, float* global_scale,
                        int64_t R, int64_t C, void* stream);
