@@ -81,6 +81,8 @@ __device__ __forceinline__ uint32_t e2m1_code(float y)
 
 // one lane = 8 consecutive elements (16 bytes) -> 8 codes (4 bytes); a block of 16 is the
 // lane pair (2b, 2b+1), whose amax is exchanged by a DPP quad permute [1,0,3,2]
+constexpr int NVFP4_QV = 2;   // two vectors per lane: 7-9% faster than one, and than four
+
 __global__ __launch_bounds__(256) void nvfp4_quant_kernel(const u32x4* __restrict__ X,
                                                           uint32_t* __restrict__ Xq,
                                                           uint8_t* __restrict__ sX,
@@ -89,52 +91,57 @@ __global__ __launch_bounds__(256) void nvfp4_quant_kernel(const u32x4* __restric
 {
     const float g = __uint_as_float(*slot);
     const float six_g = 6.0f * g;
-    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
-    const u32x4 v = i < nvec ? __builtin_nontemporal_load(&X[i]) : u32x4{0u, 0u, 0u, 0u};
-    uint32_t am = absmax_bits8(v);
-    am = max(am, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)am, 0xB1, 0xF, 0xF, false));
-    uint32_t sb = 0;
-    if (six_g != 0.0f)
-        sb = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(__uint_as_float(am << 16) / six_g, 0.0f,
-                                                      0, false) &
-             0xFFu;
-    const float D = __builtin_amdgcn_cvt_f32_fp8((int)sb, 0) * g;
-    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
-    uint32_t packed = 0;
-    if (D >= 0x1p-100f && D <= 0x1p100f) {
-        // y = fl32(x / D) without a divide per element: r = 1/D correctly rounded (one IEEE
-        // divide per lane), q = x*r, then Markstein's correction with the exact remainder
-        // x - q*D gives the correctly rounded quotient (Markstein's theorem: r within half an
-        // ulp of 1/D and q within one ulp of x/D; with the range guard, r and q stay normal
-        // and the remainder is exact wherever x/D is near an E2M1 rounding boundary, since
-        // the block scale keeps |x| < 9*D).  The E2M1 code is
-        // then the hardware convert at unit scale, which applies exactly the nearest-even,
-        // saturating rule (checked against it on every finite fp32 input).
-        const float r = 1.0f / D;
-        float y[8];
+    // NVFP4_QV vectors per lane, 256 apart (lane pairs stay aligned to 16-element blocks)
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            const float x = __uint_as_float((e & 1) ? (w[e >> 1] & 0xFFFF0000u) : (w[e >> 1] << 16));
-            const float q = x * r;
-            // negated remainder q*D - x, so that x = -0 keeps its sign: y = -0
-            y[e] = __builtin_fmaf(-__builtin_fmaf(q, D, -x), r, q);
-        }
-        packed = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(packed, y[0], y[1], 1.0f, 0);
-        packed = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(packed, y[2], y[3], 1.0f, 1);
-        packed = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(packed, y[4], y[5], 1.0f, 2);
-        packed = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(packed, y[6], y[7], 1.0f, 3);
-    } else {
+    for (int u = 0; u < NVFP4_QV; ++u) {
+        const int64_t i = (int64_t)blockIdx.x * (256 * NVFP4_QV) + u * 256 + threadIdx.x;
+        const u32x4 v = i < nvec ? __builtin_nontemporal_load(&X[i]) : u32x4{0u, 0u, 0u, 0u};
+        uint32_t am = absmax_bits8(v);
+        am = max(am, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)am, 0xB1, 0xF, 0xF, false));
+        uint32_t sb = 0;
+        if (six_g != 0.0f)
+            sb = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(__uint_as_float(am << 16) / six_g, 0.0f,
+                                                          0, false) &
+                 0xFFu;
+        const float D = __builtin_amdgcn_cvt_f32_fp8((int)sb, 0) * g;
+        const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+        uint32_t packed = 0;
+        if (D >= 0x1p-100f && D <= 0x1p100f) {
+            // y = fl32(x / D) without a divide per element: r = 1/D correctly rounded (one IEEE
+            // divide per lane), q = x*r, then Markstein's correction with the exact remainder
+            // x - q*D gives the correctly rounded quotient (Markstein's theorem: r within half an
+            // ulp of 1/D and q within one ulp of x/D; with the range guard, r and q stay normal
+            // and the remainder is exact wherever x/D is near an E2M1 rounding boundary, since
+            // the block scale keeps |x| < 9*D).  The E2M1 code is
+            // then the hardware convert at unit scale, which applies exactly the nearest-even,
+            // saturating rule (checked against it on every finite fp32 input).
+            const float r = 1.0f / D;
+            float y[8];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            const uint32_t b = (e & 1) ? (w[e >> 1] & 0xFFFF0000u) : (w[e >> 1] << 16);
-            const uint32_t c = D == 0.0f ? ((b >> 28) & 8u) : e2m1_code(__uint_as_float(b) / D);
-            packed |= c << (4 * e);
+            for (int e = 0; e < 8; ++e) {
+                const uint32_t xb = (e & 1) ? (w[e >> 1] & 0xFFFF0000u) : (w[e >> 1] << 16);
+                const float x = __uint_as_float(xb);
+                const float q = x * r;
+                // negated remainder q*D - x, so that x = -0 keeps its sign: y = -0
+                y[e] = __builtin_fmaf(-__builtin_fmaf(q, D, -x), r, q);
+            }
+            packed = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(packed, y[0], y[1], 1.0f, 0);
+            packed = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(packed, y[2], y[3], 1.0f, 1);
+            packed = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(packed, y[4], y[5], 1.0f, 2);
+            packed = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(packed, y[6], y[7], 1.0f, 3);
+        } else {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const uint32_t b = (e & 1) ? (w[e >> 1] & 0xFFFF0000u) : (w[e >> 1] << 16);
+                const uint32_t c = D == 0.0f ? ((b >> 28) & 8u) : e2m1_code(__uint_as_float(b) / D);
+                packed |= c << (4 * e);
+            }
         }
-    }
-    if (i < nvec) {
-        Xq[i] = packed;
-        if ((threadIdx.x & 1) == 0)
-            sX[i >> 1] = (uint8_t)sb;
+        if (i < nvec) {
+            Xq[i] = packed;
+            if ((threadIdx.x & 1) == 0)
+                sX[i >> 1] = (uint8_t)sb;
+        }
     }
 }
 
@@ -152,7 +159,9 @@ hipError_t launch_quant_nvfp4(const void* X, void* Xq, uint8_t* sX, float* g, in
     hipLaunchKernelGGL(nvfp4_amax_kernel, dim3((unsigned)ablocks), dim3(NVFP4_AMAX_THREADS), 0,
                        stream,
                        static_cast<const u32x4*>(X), nvec, slot);
-    hipLaunchKernelGGL(nvfp4_quant_kernel, dim3((unsigned)((nvec + 255) / 256)), dim3(256), 0,
+    hipLaunchKernelGGL(nvfp4_quant_kernel,
+                       dim3((unsigned)((nvec + 256 * NVFP4_QV - 1) / (256 * NVFP4_QV))), dim3(256),
+                       0,
                        stream, static_cast<const u32x4*>(X), static_cast<uint32_t*>(Xq), sX,
                        slot, nvec);
     return hipGetLastError();
