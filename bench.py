@@ -368,6 +368,9 @@ def cpu_baseline(A, B, step_out=None, next_out=None):
         "value": 2.0 * M * N * K / (t2 - t1) / 1e12,
         "unit": "TFLOP/s",
         "cores": nt,
+        "host_cpus": os.cpu_count(),
+        "cores_note": "threads the oracle ran on: the host's CPUs capped at 16, the CPU share "
+                      "of one GPU on the measuring box",
         "kind": "oracle",
         "sample": f"whole 4096^3 step: oracle quantize A and B ({t1 - t0:.2f} s) then fp64 "
                   f"dequantize-matmul of all {M} rows ({t2 - t1:.2f} s); value = GEMM flops "
@@ -476,10 +479,12 @@ def profile_pass(torch, fgq, synth, dev, reps=3):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    # the GPU reaches its steady clock after ~30 ms of this work (a cold start runs the
-    # first steps ~25% slower), so the default warmup is 300 steps (~50 ms)
     ap.add_argument("--steps", type=int, default=200)
-    ap.add_argument("--warmup", type=int, default=300)
+    ap.add_argument("--warmup", type=int, default=20)
+    # a cold GPU needs ~30 ms of this work to reach its steady clock (the first steps run
+    # ~25% slower), so before the --warmup steps the step is run until at least this much
+    # GPU time has passed, whatever --warmup says (reported as settle_ms / settle_steps)
+    ap.add_argument("--settle-ms", type=float, default=200.0)
     ap.add_argument("--quant-reps", type=int, default=50)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--summarize", nargs="+", metavar="DIR",
@@ -505,6 +510,7 @@ def main():
 
     import torch
     import fine_grained_block_fgq_amd as fgq
+    from fine_grained_block_fgq_amd import calib as fgq_calib
     import synth
 
     if not torch.cuda.is_available():
@@ -541,6 +547,19 @@ def main():
         if ev is not None:
             ev[1].record(stream)
 
+    # clock settle: batches of steps between two events until the GPU time adds up to
+    # --settle-ms (measured, not assumed from a step count)
+    settle_ms, settle_steps = 0.0, 0
+    s0, s1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    while settle_ms < args.settle_ms:
+        s0.record(stream)
+        for _ in range(50):
+            step()
+        s1.record(stream)
+        torch.cuda.synchronize()
+        settle_ms += s0.elapsed_time(s1)
+        settle_steps += 50
+    log(f"clock settle: {settle_steps} steps, {settle_ms:.1f} ms of GPU time")
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
@@ -595,21 +614,21 @@ def main():
     ncu = props.multi_processor_count
     cal_out = torch.empty((2 * ncu * 512,), dtype=torch.float32, device=dev)
     cal_iters = 2000
-    fgq.fgq_calib_mfma_f16(cal_out, 2 * ncu, cal_iters, stream)
+    fgq_calib.fgq_calib_mfma_f16(cal_out, 2 * ncu, cal_iters, stream)
     cev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
            for _ in range(10)]
     for a, b in cev:
         a.record(stream)
-        cal_flops = fgq.fgq_calib_mfma_f16(cal_out, 2 * ncu, cal_iters, stream)
+        cal_flops = fgq_calib.fgq_calib_mfma_f16(cal_out, 2 * ncu, cal_iters, stream)
         b.record(stream)
     torch.cuda.synchronize()
     mfma_ceiling = cal_flops / (float(np.median([a.elapsed_time(b) for a, b in cev])) * 1e-3) / 1e12
     # the same for the FP8 MFMAs (16x16x128 f8f6f4), which the GEMM does not use: what the
     # FP8 matrix cores reach here, for context next to the 5.0 PFLOP/s datasheet peak
-    fgq.fgq_calib_mfma_fp8(cal_out, 2 * ncu, cal_iters // 2, stream)
+    fgq_calib.fgq_calib_mfma_fp8(cal_out, 2 * ncu, cal_iters // 2, stream)
     for a, b in cev:
         a.record(stream)
-        cal_flops8 = fgq.fgq_calib_mfma_fp8(cal_out, 2 * ncu, cal_iters // 2, stream)
+        cal_flops8 = fgq_calib.fgq_calib_mfma_fp8(cal_out, 2 * ncu, cal_iters // 2, stream)
         b.record(stream)
     torch.cuda.synchronize()
     mfma8_ceiling = cal_flops8 / (float(np.median([a.elapsed_time(b) for a, b in cev])) * 1e-3) / 1e12
@@ -741,11 +760,11 @@ def main():
     for r, (a, b) in enumerate(sev):
         i = r % nbuf
         a.record(stream)
-        s_bytes = fgq.fgq_calib_stream(Xs[i], Xqs[i], stream)
+        s_bytes = fgq_calib.fgq_calib_stream(Xs[i], Xqs[i], stream)
         b.record(stream)
     e0.record(stream)
     for r in range(4 * nbuf):
-        fgq.fgq_calib_stream(Xs[r % nbuf], Xqs[r % nbuf], stream)
+        fgq_calib.fgq_calib_stream(Xs[r % nbuf], Xqs[r % nbuf], stream)
     e1.record(stream)
     torch.cuda.synchronize()
     s_gbs = s_bytes / (float(np.mean([a.elapsed_time(b) for a, b in sev])) * 1e-3) / 1e9
@@ -818,11 +837,13 @@ def main():
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
+        "settle_ms": round(settle_ms, 1),
+        "settle_steps": settle_steps,
         "ms_per_step": round(ms_per_step, 5),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "fp8e4m3 x fp8e4m3 -> fp32 (bf16 in/out)",
+        "dtype": "e4m3 operands, exact f16 MFMA, fp32 accumulate (bf16 in/out)",
         "data": "synthetic (Philox4x32-10 seed 0): A N(0,1), B N(0,0.02)",
         "config": {"workload": "4096^3 step: quantize A 1x128 + quantize B 128x128 + "
                                "block-scaled FP8 GEMM, bf16 C",

@@ -20,8 +20,7 @@ __all__ = [
     "fgq_quantize_act_1x128_ue8m0", "fgq_quantize_weight_128x128_ue8m0",
     "fgq_gemm_fp8_blockscaled_ue8m0", "fgq_quantize_nvfp4", "fgq_gemm_nvfp4", "FGQ_OUT_F32", "FGQ_OUT_BF16", "FGQ_GEMM_AUTO",
     "FGQ_GEMM_WIDE_256x128", "FGQ_GEMM_WIDE_128x128", "FGQ_GEMM_NARROW_64x32",
-    "FGQ_GEMM_SKINNY_128x32", "FGQ_GEMM_NARROW_64x64", "fgq_calib_stream", "fgq_calib_mfma_f16",
-    "fgq_calib_mfma_fp8", "fgq_probe_fp8_mfma_partials",
+    "FGQ_GEMM_SKINNY_128x32", "FGQ_GEMM_NARROW_64x64"
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -71,14 +70,6 @@ def load() -> ctypes.CDLL:
     lib.fgq_gemm_nvfp4.argtypes = [p, p, p, p, p, p, p, i64, i64, i64, i32, p]
     lib.fgq_gemm_fp8_blockscaled_quant.restype = i32
     lib.fgq_gemm_fp8_blockscaled_quant.argtypes = [p, p, p, p, p, p, p, i64, i64, i64, p]
-    lib.fgq_calib_stream.restype = i32
-    lib.fgq_calib_stream.argtypes = [p, p, i64, p]
-    lib.fgq_calib_mfma_f16.restype = i32
-    lib.fgq_calib_mfma_f16.argtypes = [p, i64, i64, p]
-    lib.fgq_calib_mfma_fp8.restype = i32
-    lib.fgq_calib_mfma_fp8.argtypes = [p, i64, i64, p]
-    lib.fgq_probe_fp8_mfma_partials.restype = i32
-    lib.fgq_probe_fp8_mfma_partials.argtypes = [p, p, p, i64, i64, i64, p]
     lib.fgq_status_string.restype = ctypes.c_char_p
     lib.fgq_status_string.argtypes = [i32]
     lib.fgq_version.restype = i32
@@ -312,55 +303,3 @@ def fgq_gemm_nvfp4(A_q: torch.Tensor, scale_A: torch.Tensor, global_A: torch.Ten
         _dev(global_B, "global_B", torch.float32, (1,)),
         _dev(C, "C", C.dtype, (M, N)), M, N, K, code, _stream(stream)))
     return C
-
-
-def fgq_calib_stream(src: torch.Tensor, dst: torch.Tensor, stream=None) -> int:
-    """Measured-ceiling kernel with the activation quantizer's traffic: reads all of `src`
-    (16 bytes per lane) and writes half as many bytes to `dst`.  Returns the bytes moved."""
-    lib = load()
-    if not (src.is_cuda and dst.is_cuda and src.is_contiguous() and dst.is_contiguous()):
-        raise ValueError("src and dst must be contiguous device tensors")
-    nbytes = src.numel() * src.element_size()
-    if nbytes % 16 or dst.numel() * dst.element_size() < nbytes // 2:
-        raise ValueError("src must be a multiple of 16 bytes and dst at least half its size")
-    n16 = nbytes // 16
-    _check("fgq_calib_stream", lib.fgq_calib_stream(src.data_ptr(), dst.data_ptr(), n16,
-                                                    _stream(stream)))
-    return 24 * n16
-
-
-def fgq_calib_mfma_f16(out: torch.Tensor, blocks: int, iters: int, stream=None) -> float:
-    """Measured-ceiling kernel of f16 MFMAs only; `out` float32 with blocks*512 elements.
-    Returns the flops it performs."""
-    lib = load()
-    _dev(out, "out", torch.float32, (blocks * 512,))
-    _check("fgq_calib_mfma_f16", lib.fgq_calib_mfma_f16(out.data_ptr(), blocks, iters,
-                                                        _stream(stream)))
-    return float(blocks) * 8 * iters * 16 * 16384
-
-
-def fgq_calib_mfma_fp8(out: torch.Tensor, blocks: int, iters: int, stream=None) -> float:
-    """Measured-ceiling kernel of FP8 (E4M3) MFMAs only; `out` float32 with blocks*512
-    elements.  Returns the flops it performs."""
-    lib = load()
-    _dev(out, "out", torch.float32, (blocks * 512,))
-    _check("fgq_calib_mfma_fp8", lib.fgq_calib_mfma_fp8(out.data_ptr(), blocks, iters,
-                                                        _stream(stream)))
-    return float(blocks) * 8 * iters * 16 * 65536
-
-
-def fgq_probe_fp8_mfma_partials(A_q: torch.Tensor, B_q: torch.Tensor, P: torch.Tensor = None,
-                                stream=None) -> torch.Tensor:
-    """The unscaled 128-K chunk partials of A_q [M,K] and B_q [K,N] (uint8 E4M3 codes) as
-    the FP8 matrix cores form them, one v_mfma_f32_16x16x128_f8f6f4 per 16x16 tile and chunk:
-    P [K/128, M, N] float32.  For measuring that instruction's accuracy; the GEMM entry points
-    do not use it."""
-    lib = load()
-    M, K = A_q.shape
-    N = B_q.shape[1]
-    if P is None:
-        P = torch.empty((K // 128, M, N), dtype=torch.float32, device=A_q.device)
-    _check("fgq_probe_fp8_mfma_partials", lib.fgq_probe_fp8_mfma_partials(
-        _dev(A_q, "A_q", torch.uint8, (M, K)), _dev(B_q, "B_q", torch.uint8, (K, N)),
-        _dev(P, "P", torch.float32, (K // 128, M, N)), M, N, K, _stream(stream)))
-    return P

@@ -7,7 +7,10 @@ import subprocess
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libfgq.so")
-SOURCES = ["quant.hip", "gemm.hip", "nvfp4.hip", "calib.hip", "api.cpp"]
+SOURCES = ["quant.hip", "gemm.hip", "nvfp4.hip", "api.cpp"]
+# the measurement library (ceiling kernels and the FP8-MFMA accuracy probe): not the method
+CALIB_LIB = os.path.join(HERE, "libfgq_calib.so")
+CALIB_SOURCES = ["calib.hip", "calib_api.cpp"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 FLAGS = [
@@ -20,18 +23,25 @@ FLAGS = [
 ]
 
 
-def build(verbose: bool = False) -> str:
+def _build_one(sources, lib, verbose):
     srcs = []
-    for s in SOURCES:
+    for s in sources:
         path = os.path.join(CSRC, s)
         # hipcc compiles .cpp as host code; mark every source as HIP
         srcs += ["-x", "hip", path] if s.endswith(".cpp") else [path]
-    tmp = LIB + ".tmp"
+    tmp = lib + ".tmp"
     cmd = [HIPCC, *FLAGS, *srcs, "-o", tmp]
     if verbose:
         print(" ".join(cmd))
     subprocess.check_call(cmd)
-    os.replace(tmp, LIB)
+    os.replace(tmp, lib)
+
+
+def build(verbose: bool = False) -> str:
+    """Build libfgq.so (the method) and libfgq_calib.so (measurement only); returns the
+    former's path."""
+    _build_one(SOURCES, LIB, verbose)
+    _build_one(CALIB_SOURCES, CALIB_LIB, verbose)
     return LIB
 
 

@@ -2,31 +2,17 @@
 // the gfx950 launch on the caller's stream.  No allocation, no global mutable state.
 #include "../../include/fgq.h"
 #include "fgq_launch.hpp"
+#include "api_util.hpp"
 
 #include <stdint.h>
 
 namespace {
 
+using fgq_api::launch_status;
+using fgq_api::misaligned;
+using fgq_api::overlap;
+
 constexpr int64_t kMaxDim = (int64_t(1) << 31) - 1;
-
-bool misaligned(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) != 0; }
-
-// [a, a+na) and [b, b+nb) overlap (byte ranges, empty ranges never overlap)
-bool overlap(const void* a, int64_t na, const void* b, int64_t nb)
-{
-    if (na <= 0 || nb <= 0)
-        return false;
-    const uintptr_t pa = reinterpret_cast<uintptr_t>(a), pb = reinterpret_cast<uintptr_t>(b);
-    return pa < pb + (uintptr_t)nb && pb < pa + (uintptr_t)na;
-}
-
-// a grid beyond the dispatch's 32-bit work-item count is refused before launch: a shape error
-int launch_status(hipError_t e)
-{
-    return e == hipSuccess                      ? FGQ_OK
-           : e == hipErrorInvalidConfiguration ? FGQ_ERR_SHAPE
-                                                : FGQ_ERR_LAUNCH;
-}
 
 // argument checks shared by the fp32-scale and UE8M0-scale entry points (ss: bytes per
 // scale); FGQ_OK for a valid call, including an empty one
@@ -276,64 +262,6 @@ int fgq_gemm_nvfp4(const void* A_q, const uint8_t* scale_A, const float* global_
     return launch_status(fgq::launch_gemm_nvfp4(A_q, scale_A, global_A, B_q, scale_B, global_B,
                                                 C, M, N, K, out_dtype == FGQ_OUT_BF16,
                                                 static_cast<hipStream_t>(stream)));
-}
-
-int fgq_calib_stream(const void* src, void* dst, int64_t n16, void* stream)
-{
-    if (n16 < 0 || n16 > (int64_t(1) << 34))
-        return FGQ_ERR_SHAPE;
-    if (n16 == 0)
-        return FGQ_OK;
-    if (!src || !dst)
-        return FGQ_ERR_NULL;
-    if (misaligned(src) || misaligned(dst))
-        return FGQ_ERR_ALIGN;
-    if (overlap(src, 16 * n16, dst, 8 * n16))
-        return FGQ_ERR_ALIAS;
-    return launch_status(fgq::launch_calib_stream(src, dst, n16, static_cast<hipStream_t>(stream)));
-}
-
-int fgq_calib_mfma_f16(float* out, int64_t blocks, int64_t iters, void* stream)
-{
-    if (blocks < 1 || blocks > (int64_t(1) << 20) || iters < 0 || iters > (int64_t(1) << 24))
-        return FGQ_ERR_SHAPE;
-    if (!out)
-        return FGQ_ERR_NULL;
-    if (misaligned(out))
-        return FGQ_ERR_ALIGN;
-    return launch_status(
-        fgq::launch_calib_mfma_f16(out, blocks, iters, static_cast<hipStream_t>(stream)));
-}
-
-int fgq_calib_mfma_fp8(float* out, int64_t blocks, int64_t iters, void* stream)
-{
-    if (blocks < 1 || blocks > (int64_t(1) << 20) || iters < 0 || iters > (int64_t(1) << 24))
-        return FGQ_ERR_SHAPE;
-    if (!out)
-        return FGQ_ERR_NULL;
-    if (misaligned(out))
-        return FGQ_ERR_ALIGN;
-    return launch_status(
-        fgq::launch_calib_mfma_fp8(out, blocks, iters, static_cast<hipStream_t>(stream)));
-}
-
-int fgq_probe_fp8_mfma_partials(const void* A_q, const void* B_q, float* P, int64_t M,
-                                int64_t N, int64_t K, void* stream)
-{
-    if (M < 0 || N < 0 || K < 0 || M % 16 || N % 16 || K % 128 || M > (int64_t(1) << 16) ||
-        N > (int64_t(1) << 16) || K > (int64_t(1) << 16))
-        return FGQ_ERR_SHAPE;
-    if (M == 0 || N == 0 || K == 0)
-        return FGQ_OK;
-    if (!A_q || !B_q || !P)
-        return FGQ_ERR_NULL;
-    if (misaligned(A_q) || misaligned(B_q) || misaligned(P))
-        return FGQ_ERR_ALIGN;
-    const int64_t np = (K / 128) * M * N * 4;
-    if (overlap(P, np, A_q, M * K) || overlap(P, np, B_q, K * N))
-        return FGQ_ERR_ALIAS;
-    return launch_status(fgq::launch_probe_fp8_mfma_partials(A_q, B_q, P, M, N, K,
-                                                             static_cast<hipStream_t>(stream)));
 }
 
 }  // extern "C"

@@ -1,27 +1,26 @@
-// calib.hip -- measured ceilings for the roofline fractions (measurement only, not a step of
-// the method).  Datasheet peaks are not reachable on a real box; these two kernels give what
-// plain code of the same shape gets, next to which the quantizer and the GEMM are judged:
+// calib.hip -- kernels of libfgq_calib, the measurement library (not a step of the method).
+// Datasheet peaks are not reachable on a real box; these kernels give what plain code of the
+// same shape gets, next to which the quantizer and the GEMM are judged, and measure the FP8
+// matrix cores' own accuracy:
 //
 //   calib_stream: the activation quantizer's traffic with no arithmetic -- every lane reads
-//     16 bytes and writes 8, non-temporal, two loads in flight per lane.  Page "Asynchronous
-//     Data Copies (LDGSTS)", section on maximizing memory bandwidth: bandwidth is reached by
-//     keeping enough bytes in flight, and a vanilla elementwise kernel is the reference.
+//     16 bytes and writes 8, non-temporal, two loads in flight per lane.
 //   calib_mfma_f16: only v_mfma_f32_16x16x32_f16, the instruction the GEMM's partials use, in
-//     four independent accumulation chains per wave on register operands, two waves per SIMD.
-//     Page "Instruction-Level Parallelism (ILP)": independent chains are what let a pipelined
-//     unit reach its issue rate.
+//     four independent accumulation chains per wave on register operands, two waves per SIMD,
+//     so that the matrix cores run at their issue rate.
 //   calib_mfma_fp8: the same with v_mfma_f32_16x16x128_f8f6f4 on E4M3 operands: what the FP8
 //     matrix cores reach on this GPU.
 //   probe_fp8_mfma_partials: the 128-K chunk partials sum_k A_q[m,k] * B_q[k,n] formed by one
 //     v_mfma_f32_16x16x128_f8f6f4 per 16x16 tile and chunk, written out unscaled, so that their
-//     error against the exact sums can be measured (page "Fine-Grained FP8/FP4 Quantization",
-//     section "Hopper: CUDA Core Promotion (Nc=128)": the FP8 tensor-core sum is kept at reduced
-//     precision, which is why the method promotes every 128 K; on gfx950 the reduced precision
-//     is inside each instruction, so the GEMM forms its partials with f16 MFMAs instead).
+//     error against the exact sums can be measured.  The method promotes every 128-K partial
+//     to fp32 because FP8 tensor-core sums are kept at reduced precision (page "Fine-Grained
+//     FP8/FP4 Quantization", section "Hopper: CUDA Core Promotion (Nc=128)"); on gfx950 the
+//     reduced precision is inside each FP8 instruction, so the GEMM forms its partials with
+//     f16 MFMAs instead.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
-#include "fgq_launch.hpp"
+#include "calib_launch.hpp"
 
 namespace fgq {
 

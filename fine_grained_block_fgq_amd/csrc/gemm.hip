@@ -32,6 +32,7 @@
 #include "gemm_common.hpp"
 
 #include <atomic>
+#include <type_traits>
 
 // compile-time tuning knobs (defaults are the shipped configuration)
 #ifndef FGQ_SCHED
@@ -111,9 +112,15 @@ struct GemmCfg {
 
 // Scale formats the GEMM reads: fp32 scales, or UE8M0 exponent bytes e standing for
 // 2^(e-127) (page "Fine-Grained FP8/FP4 Quantization", section "Blackwell: Native Block
-// Scaling").  Either way one 4-byte LDS slot per tile row carries scale_A of the chunk, and
-// the combined scale of a row is formed in fp32: sA*sB, or 2^(eA-127) * 2^(eB-127) by an
-// exponent add (exact unless it falls below the fp32 range).
+// Scaling").  Either way one 4-byte LDS slot per tile row carries scale_A of the chunk.
+// The scaled partial P*sA*sB is formed without an overflow that C itself would not have:
+//   sB <= 1: acc = fma(P, sA*sB, acc) -- the combined scale is at most sA, so it cannot
+//            overflow (an underflow of it costs less than 2^-149 * |P|, far below the
+//            tolerance's absolute term);
+//   sB >  1: acc = fma(P*sA, sB, acc) -- P*sA can only overflow where P*sA*sB, a term of C,
+//            lies beyond the fp32 range anyway.
+// sB is uniform over a wave, so the choice is a scalar branch per chunk (row()/combine()
+// give the per-row factor of each form).
 template <bool E8>
 struct ScaleIn;
 template <>
@@ -125,6 +132,10 @@ struct ScaleIn<false> {
     {
         return *(const f32x4 LDS*)p * sb;
     }
+    static __device__ __forceinline__ f32x4 row(const uint8_t LDS* p)
+    {
+        return *(const f32x4 LDS*)p;
+    }
 };
 template <>
 struct ScaleIn<true> {
@@ -134,11 +145,17 @@ struct ScaleIn<true> {
     {
         return __builtin_ldexpf(1.0f, (int)e - 127);
     }
+    // 2^(eA-127) * sB by an exponent add: exact unless it falls below the fp32 range
     static __device__ __forceinline__ f32x4 combine(const uint8_t LDS* p, float sb)
     {
         const i32x4 e = *(const i32x4 LDS*)p;
         return f32x4{__builtin_ldexpf(sb, e[0] - 127), __builtin_ldexpf(sb, e[1] - 127),
                      __builtin_ldexpf(sb, e[2] - 127), __builtin_ldexpf(sb, e[3] - 127)};
+    }
+    // 2^(eA-127) itself (exact in fp32 for every byte 0..254)
+    static __device__ __forceinline__ f32x4 row(const uint8_t LDS* p)
+    {
+        return combine(p, 1.0f);
     }
 };
 
@@ -320,17 +337,18 @@ struct NoLoader {
 // stage between its column blocks).  The chunk's combined scales and the wave's A operands
 // are read and converted once; then per column block j the B operands, four chained f16
 // MFMAs per tile, and acc += P * (sA*sB).
-template <class Cfg, class SI, class Loader = NoLoader>
-__device__ __forceinline__ void compute_chunk(const uint8_t LDS* cur, const FragOffsets<Cfg>& fo,
-                                              int s_off, float sb,
-                                              f32x4 (&acc)[Cfg::FM][Cfg::FN],
-                                              const Loader& loader = Loader())
+template <class Cfg, class SI, bool BIG_SB, class Loader>
+__device__ __forceinline__ void compute_chunk_impl(const uint8_t LDS* cur,
+                                                   const FragOffsets<Cfg>& fo, int s_off, float sb,
+                                                   f32x4 (&acc)[Cfg::FM][Cfg::FN],
+                                                   const Loader& loader)
 {
-    // combined scales for this lane's rows: sA[row, kb] * sB[kb, nb]
+    // per-row factors for this lane's rows: sA[row, kb] * sB[kb, nb], or sA alone when
+    // sB > 1 (then sB multiplies after sA, see ScaleIn)
     f32x4 cs[Cfg::FM];
 #pragma unroll
     for (int i = 0; i < Cfg::FM; ++i)
-        cs[i] = SI::combine(cur + s_off + i * 64, sb);
+        cs[i] = BIG_SB ? SI::row(cur + s_off + i * 64) : SI::combine(cur + s_off + i * 64, sb);
     // A operands: lane bytes 8t..8t+7 of its 32 (k = 32g + 8t + b) -> sub-step t
     i32x4 araw[Cfg::FM][2];
 #pragma unroll
@@ -378,7 +396,8 @@ __device__ __forceinline__ void compute_chunk(const uint8_t LDS* cur, const Frag
         for (int i = 0; i < Cfg::FM; ++i)
 #pragma unroll
             for (int r = 0; r < 4; ++r)
-                acc[i][j][r] = __builtin_fmaf(p[i][r], cs[i][r], acc[i][j][r]);
+                acc[i][j][r] = BIG_SB ? __builtin_fmaf(p[i][r] * cs[i][r], sb, acc[i][j][r])
+                                      : __builtin_fmaf(p[i][r], cs[i][r], acc[i][j][r]);
     }
 #if FGQ_SCHED == 1
     __builtin_amdgcn_iglp_opt(0);
@@ -386,6 +405,45 @@ __device__ __forceinline__ void compute_chunk(const uint8_t LDS* cur, const Frag
     __builtin_amdgcn_iglp_opt(1);
 #endif
 }
+
+// one chunk in the scale form of the loop it belongs to (BIG_SB: some sB of the wave > 1)
+template <class Cfg, class SI, bool BIG_SB, class Loader = NoLoader>
+__device__ __forceinline__ void compute_chunk(const uint8_t LDS* cur, const FragOffsets<Cfg>& fo,
+                                              int s_off, float sb,
+                                              f32x4 (&acc)[Cfg::FM][Cfg::FN],
+                                              const Loader& loader = Loader())
+{
+    compute_chunk_impl<Cfg, SI, BIG_SB>(cur, fo, s_off, sb, acc, loader);
+}
+
+// Whether any of the n scale_B values p[i * stride] (i < n) a wave uses exceeds 1, as a
+// wave-uniform flag: the wave then runs its K loop in the overflow-safe form (see ScaleIn).
+// The first 64 values are loaded by the constructor, one per lane, before the kernel's
+// prologue loads, so that their latency hides under those; any() reads the rest (K beyond
+// 64 chunks per wave) and votes.
+template <class SI>
+struct ScaleBFlag {
+    const typename SI::T* __restrict__ p;
+    int64_t stride, n;
+    int lane;
+    float first;
+    __device__ __forceinline__ ScaleBFlag(const typename SI::T* __restrict__ p_, int64_t stride_,
+                                          int64_t n_, int lane_)
+        : p(p_), stride(stride_), n(n_), lane(lane_),
+          first(lane_ < n_ ? SI::value(p_[lane_ * stride_]) : 0.0f)
+    {
+    }
+    __device__ __forceinline__ bool any_above_one() const
+    {
+        bool big = first > 1.0f;
+        for (int64_t i0 = 64; i0 < n; i0 += 64) {
+            const int64_t i = i0 + lane;
+            if (i < n && SI::value(p[i * stride]) > 1.0f)
+                big = true;
+        }
+        return __builtin_amdgcn_ballot_w64(big) != 0;
+    }
+};
 
 // Fused epilogue: the tile's bf16 results are staged in LDS, then every 1x128 row group is
 // written to C and quantized exactly as the activation quantizer does it (same amax, scale
@@ -439,8 +497,11 @@ __device__ __forceinline__ void store_quant_tile(uint8_t LDS* smem,
     }
 }
 
+// two waves per SIMD (the 128x128 tiles' 4 waves leave room for two workgroups per CU only if
+// a wave keeps within 256 registers)
 template <class Cfg, class SI, bool OUT_BF16, bool FUSE = false>
-__global__ __launch_bounds__(Cfg::NT) void gemm_fp8_blockscaled_kernel(
+__global__ __launch_bounds__(Cfg::NT) __attribute__((amdgpu_waves_per_eu(2)))
+void gemm_fp8_blockscaled_kernel(
     const uint8_t* __restrict__ A, const typename SI::T* __restrict__ sA,
     const uint8_t* __restrict__ B, const typename SI::T* __restrict__ sB,
     void* __restrict__ Cout, int64_t M, int64_t N, int64_t K, int64_t n_begin, int64_t n_end,
@@ -491,8 +552,9 @@ __global__ __launch_bounds__(Cfg::NT) void gemm_fp8_blockscaled_kernel(
         for (int j = 0; j < Cfg::FN; ++j)
             acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-    // scale_B of the wave's column block, chunk by chunk
+    // scale_B of the wave's column block, chunk by chunk (and whether any of it exceeds 1)
     ScaleBWalk<SI> sbw(sB + (nb_wave < NB ? nb_wave : NB - 1), NB, KB, lane);
+    const ScaleBFlag<SI> sbf(sB + (nb_wave < NB ? nb_wave : NB - 1), NB, KB, lane);
 
     // prologue: the first STAGES-1 chunks in flight
 #pragma unroll
@@ -500,35 +562,43 @@ __global__ __launch_bounds__(Cfg::NT) void gemm_fp8_blockscaled_kernel(
         if (st < KB)
             load_stage<Cfg, SI>(smem + st * Cfg::STAGE, A, sA, B, M, N, K, m0, n0, st, wave, lane);
 
-    for (int64_t kb = 0; kb < KB; ++kb) {
-        const uint8_t LDS* cur = smem + (kb % Cfg::STAGES) * Cfg::STAGE;
-        // chunk kb has landed once only the later chunks' loads may still be outstanding
-        // (chunks kb+1 .. kb+STAGES-2, those already issued)
-        const int64_t later = (KB - 1 - kb) < (Cfg::STAGES - 2) ? (KB - 1 - kb) : (Cfg::STAGES - 2);
-        if (Cfg::STAGES >= 4 && later >= 2)
-            wait_vm<2 * Cfg::MIN_LOADS>();
-        else if (Cfg::STAGES >= 3 && later >= 1)
-            wait_vm<Cfg::MIN_LOADS>();
-        else
-            wait_vm<0>();
-        // all waves: chunk kb visible, and chunk kb-1 fully read (its buffer may refill)
-        lds_barrier();
-        const int64_t nxt = kb + Cfg::STAGES - 1;
+    // the K loop, in the scale form the wave's scale_B values call for
+    auto k_loop = [&](auto big_tag) {
+        constexpr bool BIG = decltype(big_tag)::value;
+        for (int64_t kb = 0; kb < KB; ++kb) {
+            const uint8_t LDS* cur = smem + (kb % Cfg::STAGES) * Cfg::STAGE;
+            // chunk kb has landed once only the later chunks' loads may still be outstanding
+            // (chunks kb+1 .. kb+STAGES-2, those already issued)
+            const int64_t later = (KB - 1 - kb) < (Cfg::STAGES - 2) ? (KB - 1 - kb) : (Cfg::STAGES - 2);
+            if (Cfg::STAGES >= 4 && later >= 2)
+                wait_vm<2 * Cfg::MIN_LOADS>();
+            else if (Cfg::STAGES >= 3 && later >= 1)
+                wait_vm<Cfg::MIN_LOADS>();
+            else
+                wait_vm<0>();
+            // all waves: chunk kb visible, and chunk kb-1 fully read (its buffer may refill)
+            lds_barrier();
+            const int64_t nxt = kb + Cfg::STAGES - 1;
 #if FGQ_SPREAD_DMA
-        // chunk nxt's loads go out a few at a time between this chunk's column blocks
-        const StageLoader<Cfg, SI> loader{smem + (nxt % Cfg::STAGES) * Cfg::STAGE, A, sA, B, M, N,
-                                          K, m0, n0, nxt, wave, lane, nxt < KB};
+            // chunk nxt's loads go out a few at a time between this chunk's column blocks
+            const StageLoader<Cfg, SI> loader{smem + (nxt % Cfg::STAGES) * Cfg::STAGE, A, sA, B, M, N,
+                                              K, m0, n0, nxt, wave, lane, nxt < KB};
 #else
-        if (nxt < KB)
-            load_stage<Cfg, SI>(smem + (nxt % Cfg::STAGES) * Cfg::STAGE, A, sA, B, M, N, K, m0, n0,
-                            nxt, wave, lane);
-        const NoLoader loader;
+            if (nxt < KB)
+                load_stage<Cfg, SI>(smem + (nxt % Cfg::STAGES) * Cfg::STAGE, A, sA, B, M, N, K, m0, n0,
+                                nxt, wave, lane);
+            const NoLoader loader;
 #endif
-        const float sb = sbw.get(kb);
-        compute_chunk<Cfg, SI>(cur, fo, s_off, sb, acc, loader);
-        if (Cfg::STAGES == 2)
-            lds_barrier();   // keeps the waves in step (measured faster than letting them drift)
-    }
+            const float sb = sbw.get(kb);
+            compute_chunk<Cfg, SI, BIG>(cur, fo, s_off, sb, acc, loader);
+            if (Cfg::STAGES == 2)
+                lds_barrier();   // keeps the waves in step (measured faster than letting them drift)
+        }
+    };
+    if (sbf.any_above_one())
+        k_loop(std::true_type{});
+    else
+        k_loop(std::false_type{});
 
     static_assert(!FUSE || Cfg::BN >= 128, "the fused epilogue needs whole 128-column groups");
     if constexpr (STAGED) {
@@ -635,37 +705,46 @@ __global__ __launch_bounds__(Cfg::NT * KG) void gemm_fp8_blockscaled_ksplit_kern
 
     // this group's chunk of step s is kb = s*KG + kg (if < KB)
     ScaleBWalk<SI> sbw(sB + kg * NB + nb, KG * NB, kg < KB ? (KB - kg + KG - 1) / KG : 0, lane);
+    const ScaleBFlag<SI> sbf(sB + kg * NB + nb, KG * NB, kg < KB ? (KB - kg + KG - 1) / KG : 0,
+                             lane);
     auto stage_of = [&](int64_t st) { return smem + ((st % Cfg::STAGES) * KG + kg) * Cfg::STAGE; };
 #pragma unroll
     for (int st = 0; st < Cfg::STAGES - 1; ++st)
         if (st < steps && st * KG + kg < KB)
             load_stage<Cfg, SI>(stage_of(st), A, sA, B, M, N, K, m0, n0, st * KG + kg, wl, lane);
 
-    for (int64_t st = 0; st < steps; ++st) {
-        const int64_t kb = st * KG + kg;
-        // this wave's own loads issued for later steps (chunk present in those steps)
-        int later = 0;
-#pragma unroll
-        for (int d = 1; d <= Cfg::STAGES - 2; ++d)
-            later += (st + d < steps && (st + d) * KG + kg < KB) ? 1 : 0;
-        if (Cfg::STAGES >= 4 && later >= 2)
-            wait_vm<2 * Cfg::MIN_LOADS>();
-        else if (Cfg::STAGES >= 3 && later >= 1)
-            wait_vm<Cfg::MIN_LOADS>();
-        else
-            wait_vm<0>();
-        lds_barrier();   // step st visible to all; step st-1 fully read (its stage refills)
-        const int64_t nxt = st + Cfg::STAGES - 1;
-        if (nxt < steps && nxt * KG + kg < KB)
-            load_stage<Cfg, SI>(stage_of(nxt), A, sA, B, M, N, K, m0, n0, nxt * KG + kg, wl,
-                                lane);
-        if (kb < KB) {
-            const float sb = sbw.get(st);
-            compute_chunk<Cfg, SI>(stage_of(st), fo, s_off, sb, acc);
+    auto k_loop = [&](auto big_tag) {
+        constexpr bool BIG = decltype(big_tag)::value;
+        for (int64_t st = 0; st < steps; ++st) {
+            const int64_t kb = st * KG + kg;
+            // this wave's own loads issued for later steps (chunk present in those steps)
+            int later = 0;
+    #pragma unroll
+            for (int d = 1; d <= Cfg::STAGES - 2; ++d)
+                later += (st + d < steps && (st + d) * KG + kg < KB) ? 1 : 0;
+            if (Cfg::STAGES >= 4 && later >= 2)
+                wait_vm<2 * Cfg::MIN_LOADS>();
+            else if (Cfg::STAGES >= 3 && later >= 1)
+                wait_vm<Cfg::MIN_LOADS>();
+            else
+                wait_vm<0>();
+            lds_barrier();   // step st visible to all; step st-1 fully read (its stage refills)
+            const int64_t nxt = st + Cfg::STAGES - 1;
+            if (nxt < steps && nxt * KG + kg < KB)
+                load_stage<Cfg, SI>(stage_of(nxt), A, sA, B, M, N, K, m0, n0, nxt * KG + kg, wl,
+                                    lane);
+            if (kb < KB) {
+                const float sb = sbw.get(st);
+                compute_chunk<Cfg, SI, BIG>(stage_of(st), fo, s_off, sb, acc);
+            }
+            if (Cfg::STAGES == 2)
+                lds_barrier();
         }
-        if (Cfg::STAGES == 2)
-            lds_barrier();
-    }
+    };
+    if (sbf.any_above_one())
+        k_loop(std::true_type{});
+    else
+        k_loop(std::false_type{});
 
     // sum the KG partial tiles in group order
     lds_barrier();
@@ -845,27 +924,36 @@ __global__ __launch_bounds__(Cfg::NT) void gemm_fp8_blockscaled_narrow_kernel(
     // this wave's chunks: kb = wave + c*KW, c < nc
     const int64_t nc = wave < KB ? (KB - wave + Cfg::KW - 1) / Cfg::KW : 0;
     ScaleBWalk<SI> sbw(sB + wave * NB + nb, Cfg::KW * NB, nc, lane);
+    const ScaleBFlag<SI> sbf(sB + wave * NB + nb, Cfg::KW * NB, nc, lane);
 #pragma unroll
     for (int st = 0; st < Cfg::STAGES - 1; ++st)
         if (st < nc)
             narrow_load<Cfg, SI>(ring + st * Cfg::STAGE, A, sA, B, M, N, K, m0, n0,
                              wave + st * Cfg::KW, lane);
-    for (int64_t c = 0; c < nc; ++c) {
-        // chunk c has landed once only the next chunk's loads may be outstanding; every
-        // LDS read of the previous chunk has returned (its stage is refilled next)
-        if (Cfg::STAGES == 3 && c + 1 < nc)
-            wait_vm<Cfg::LOADS>();
-        else
-            wait_vm<0>();
-        __builtin_amdgcn_s_waitcnt(0xC07F);
-        asm volatile("" ::: "memory");
-        const int64_t nxt = c + Cfg::STAGES - 1;
-        if (nxt < nc)
-            narrow_load<Cfg, SI>(ring + (nxt % Cfg::STAGES) * Cfg::STAGE, A, sA, B, M, N, K, m0,
-                             n0, wave + nxt * Cfg::KW, lane);
-        const float sb = sbw.get(c);
-        compute_chunk<Cfg, SI>(ring + (c % Cfg::STAGES) * Cfg::STAGE, fo, s_off, sb, acc);
-    }
+    auto k_loop = [&](auto big_tag) {
+        constexpr bool BIG = decltype(big_tag)::value;
+        for (int64_t c = 0; c < nc; ++c) {
+            // chunk c has landed once only the next chunk's loads may be outstanding; every
+            // LDS read of the previous chunk has returned (its stage is refilled next)
+            if (Cfg::STAGES == 3 && c + 1 < nc)
+                wait_vm<Cfg::LOADS>();
+            else
+                wait_vm<0>();
+            __builtin_amdgcn_s_waitcnt(0xC07F);
+            asm volatile("" ::: "memory");
+            const int64_t nxt = c + Cfg::STAGES - 1;
+            if (nxt < nc)
+                narrow_load<Cfg, SI>(ring + (nxt % Cfg::STAGES) * Cfg::STAGE, A, sA, B, M, N, K, m0,
+                                 n0, wave + nxt * Cfg::KW, lane);
+            const float sb = sbw.get(c);
+            compute_chunk<Cfg, SI, BIG>(ring + (c % Cfg::STAGES) * Cfg::STAGE, fo, s_off, sb,
+                                         acc);
+        }
+    };
+    if (sbf.any_above_one())
+        k_loop(std::true_type{});
+    else
+        k_loop(std::false_type{});
 
     // sum the KW partial tiles in wave order, then store coalesced
     __syncthreads();

@@ -383,8 +383,13 @@ __global__ __launch_bounds__(Cfg::NT * KG) void gemm_nvfp4_kernel(
                                                                 PER_LANE +
                                                             (i * Cfg::FN + j) * 4));
     }
-    // lane holds C[16i + 4g + r][16j + q] of the wave tile
-    const float gab = *gA * *gB;
+    // lane holds C[16i + 4g + r][16j + q] of the wave tile.  The two global scales multiply
+    // as mantissas (each in [0.5, 1)) and one exponent applied last by ldexp, so the product
+    // gA*gB cannot overflow where C itself is finite.
+    int ea = 0, eb = 0;
+    const float ma = frexpf(*gA, &ea), mb = frexpf(*gB, &eb);
+    const float gm = ma * mb;
+    const int ge = ea + eb;
 #pragma unroll
     for (int i = 0; i < Cfg::FM; ++i)
 #pragma unroll
@@ -395,7 +400,7 @@ __global__ __launch_bounds__(Cfg::NT * KG) void gemm_nvfp4_kernel(
 #pragma unroll
             for (int j = 0; j < Cfg::FN; ++j) {
                 const int64_t col = n0 + wn * Cfg::TN + 16 * j + q;
-                const float v = acc[i][j][r] * gab;
+                const float v = ldexpf(acc[i][j][r] * gm, ge);
                 if (OUT_BF16)
                     static_cast<__bf16*>(Cout)[row * N + col] = (__bf16)v;
                 else

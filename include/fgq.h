@@ -191,47 +191,6 @@ int fgq_gemm_nvfp4(const void* A_q, const uint8_t* scale_A, const float* global_
                    const void* B_q, const uint8_t* scale_B, const float* global_B, void* C,
                    int64_t M, int64_t N, int64_t K, int out_dtype, void* stream);
 
-/*
- * Measured ceilings for the roofline fractions (measurement only; not steps of the method).
- * Datasheet peaks are not reachable by real code; these give what plain kernels of the same
- * shape reach on the running GPU.
- *
- * fgq_calib_stream: the activation quantizer's memory traffic with no arithmetic (page
- * "Asynchronous Data Copies (LDGSTS)", maximizing memory bandwidth: the reference is a vanilla
- * elementwise kernel with enough bytes in flight).  For i < n16 it reads the 16 bytes at
- * src + 16*i and writes 8 bytes (an XOR of its words) at dst + 8*i.
- *   src  in: device, n16*16 bytes, 16-byte aligned     dst  out: device, n16*8 bytes
- * Errors: FGQ_ERR_SHAPE (n16 < 0 or too large), FGQ_ERR_NULL, FGQ_ERR_ALIGN, FGQ_ERR_ALIAS.
- *
- * fgq_calib_mfma_f16: only f16 MFMAs (v_mfma_f32_16x16x32_f16, the GEMM's instruction) in
- * independent accumulation chains, `blocks` workgroups of 8 waves (page "Instruction-Level
- * Parallelism (ILP)": independent chains reach a pipelined unit's issue rate).  Work:
- * blocks * 8 * iters * 16 MFMAs of 16384 flop each.  `out` (device, blocks*512 floats) gets
- * a checksum per thread.  Errors: FGQ_ERR_SHAPE (blocks outside [1, 2^20] or iters outside
- * [0, 2^24]), FGQ_ERR_NULL, FGQ_ERR_ALIGN.
- *
- * fgq_calib_mfma_fp8: the same with FP8 (E4M3) MFMAs (v_mfma_f32_16x16x128_f8f6f4): what the
- * FP8 matrix cores reach.  Work: blocks * 8 * iters * 16 MFMAs of 65536 flop each.  Same
- * arguments and errors as fgq_calib_mfma_f16.
- *
- * fgq_probe_fp8_mfma_partials: the 128-K chunk partials P[kb][m][n] = sum over the chunk of
- * A_q[m,k] * B_q[k,n], each formed by one FP8 MFMA (v_mfma_f32_16x16x128_f8f6f4) per 16x16
- * tile, unscaled.  It shows how far the FP8 matrix cores' own sum is from the exact one (page
- * "Fine-Grained FP8/FP4 Quantization", section "Hopper: CUDA Core Promotion (Nc=128)": the
- * FP8 tensor-core sum is kept at reduced precision, hence the promotion every 128 K); the GEMM
- * entry points do not use it.
- *   A_q  in: device, E4M3 [M, K] row-major, 16-byte aligned
- *   B_q  in: device, E4M3 [K, N] row-major (N contiguous)
- *   P    out: device, fp32 [K/128, M, N], overwritten
- * M and N multiples of 16, K of 128, each at most 65536; any of them 0: no-op.
- * Errors: FGQ_ERR_SHAPE, FGQ_ERR_NULL, FGQ_ERR_ALIGN, FGQ_ERR_ALIAS (P overlaps an input).
- */
-int fgq_calib_stream(const void* src, void* dst, int64_t n16, void* stream);
-int fgq_calib_mfma_f16(float* out, int64_t blocks, int64_t iters, void* stream);
-int fgq_calib_mfma_fp8(float* out, int64_t blocks, int64_t iters, void* stream);
-int fgq_probe_fp8_mfma_partials(const void* A_q, const void* B_q, float* P, int64_t M,
-                                int64_t N, int64_t K, void* stream);
-
 /* Static text for a status code. */
 const char* fgq_status_string(int status);
 

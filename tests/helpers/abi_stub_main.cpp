@@ -1,4 +1,4 @@
-// Host-only check of libfgq's C ABI layer (api.cpp) with the kernel launchers replaced by
+// Host-only check of the C ABI layers of libfgq (api.cpp) and libfgq_calib (calib_api.cpp) with the kernel launchers replaced by
 // stubs: every entry point with valid arguments reaches its launcher exactly once and
 // passes the launcher's status through (hipSuccess -> FGQ_OK, a launch failure ->
 // FGQ_ERR_LAUNCH, a grid the dispatch cannot count -> FGQ_ERR_SHAPE); invalid arguments
@@ -8,6 +8,8 @@
 #include <cstdlib>
 
 #include "../../include/fgq.h"
+#include "../../include/fgq_calib.h"
+#include "../../fine_grained_block_fgq_amd/csrc/calib_launch.hpp"
 #include "../../fine_grained_block_fgq_amd/csrc/fgq_launch.hpp"
 
 namespace {

@@ -8,13 +8,15 @@ import re
 import pytest
 
 import fine_grained_block_fgq_amd as fgq
+from fine_grained_block_fgq_amd import calib
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "fgq.h")
+CALIB_HEADER = os.path.join(ROOT, "include", "fgq_calib.h")
 
 
-def declared_functions():
-    text = open(HEADER).read()
+def declared_functions(header=HEADER):
+    text = open(header).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
     return sorted(set(re.findall(r"\b(fgq_[a-z0-9_]+)\s*\(", text)))
 
@@ -27,6 +29,21 @@ def test_library_exports_declared_symbols():
     for n in names:
         assert hasattr(lib, n), n
     assert lib.fgq_version() >= 100
+
+
+def test_measurement_library_is_separate():
+    """The measurement-only kernels live in libfgq_calib (include/fgq_calib.h), not in the
+    method's library"""
+    lib = calib.load()
+    names = declared_functions(CALIB_HEADER)
+    assert set(names) == {"fgq_calib_stream", "fgq_calib_mfma_f16", "fgq_calib_mfma_fp8",
+                          "fgq_probe_fp8_mfma_partials"}
+    for n in names:
+        assert hasattr(lib, n), n
+    main = set(declared_functions())
+    assert not (main & set(names))
+    for n in names:
+        assert not hasattr(fgq.load(), n), n
 
 
 def test_status_strings():
@@ -176,7 +193,7 @@ def test_nvfp4_validation(fn, args, want):
     ("fgq_probe_fp8_mfma_partials", (None, None, None, 0, 16, 128), 0),
 ])
 def test_calib_validation(fn, args, want):
-    assert getattr(fgq.load(), fn)(*args, None) == want
+    assert getattr(calib.load(), fn)(*args, None) == want
 
 
 # Shapes that pass the argument checks but whose grid would exceed the 2^32 work-items one
@@ -221,7 +238,7 @@ def test_binding_refuses_host_tensors():
                                                    _host((128, 128), u8), _host((1, 1), u8)),
         lambda: fgq.fgq_gemm_nvfp4(_host((4, 64), u8), _host((4, 8), u8), _host((1,), f32),
                                    _host((128, 64), u8), _host((128, 8), u8), _host((1,), f32)),
-        lambda: fgq.fgq_probe_fp8_mfma_partials(_host((16, 128), u8), _host((128, 16), u8)),
+        lambda: calib.fgq_probe_fp8_mfma_partials(_host((16, 128), u8), _host((128, 16), u8)),
     ]
     for i, call in enumerate(calls):
         with pytest.raises(TypeError, match="CUDA"):

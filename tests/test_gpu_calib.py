@@ -1,4 +1,4 @@
-"""The measurement-only ceiling kernels (libfgq's fgq_calib_stream / fgq_calib_mfma_f16) do
+"""The measurement-only ceiling kernels (libfgq_calib's fgq_calib_stream / fgq_calib_mfma_f16) do
 what bench.py assumes: the stream touches every input byte and writes the word XORs, and the
 MFMA kernel runs to completion with a repeatable result."""
 import numpy as np
@@ -6,6 +6,7 @@ import pytest
 import torch
 
 import fine_grained_block_fgq_amd as fgq
+from fine_grained_block_fgq_amd import calib
 
 pytestmark = pytest.mark.gpu
 
@@ -17,7 +18,7 @@ def test_calib_stream_writes_word_xors(n16):
     src_h = rng.integers(0, 2**32, size=4 * n16, dtype=np.uint32)
     src = torch.from_numpy(src_h.view(np.int32)).cuda()
     dst = torch.full((2 * n16 + 2,), -1, dtype=torch.int32, device="cuda")
-    moved = fgq.fgq_calib_stream(src, dst)
+    moved = calib.fgq_calib_stream(src, dst)
     torch.cuda.synchronize()
     assert moved == 24 * n16
     got = dst.cpu().numpy().view(np.uint32)
@@ -30,11 +31,11 @@ def test_calib_stream_writes_word_xors(n16):
 def test_calib_mfma_runs_and_repeats():
     print("calib_mfma blocks=8 iters=5", flush=True)
     out = torch.zeros((8 * 512,), dtype=torch.float32, device="cuda")
-    flops = fgq.fgq_calib_mfma_f16(out, 8, 5)
+    flops = calib.fgq_calib_mfma_f16(out, 8, 5)
     torch.cuda.synchronize()
     assert flops == 8 * 8 * 5 * 16 * 16384
     first = out.clone()
-    fgq.fgq_calib_mfma_f16(out, 8, 5)
+    calib.fgq_calib_mfma_f16(out, 8, 5)
     torch.cuda.synchronize()
     assert torch.isfinite(first).all()
     assert torch.equal(first, out)

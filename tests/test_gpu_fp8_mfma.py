@@ -1,6 +1,6 @@
 """Why the GEMM forms its 128-K chunk partials with f16 MFMAs on exactly converted operands
 instead of the FP8 MFMAs: on the workloads' own codes the FP8 matrix core's sum
-(v_mfma_f32_16x16x128_f8f6f4, reached through libfgq's fgq_probe_fp8_mfma_partials) misses
+(v_mfma_f32_16x16x128_f8f6f4, reached through libfgq_calib's fgq_probe_fp8_mfma_partials) misses
 the required |C - C_ref| <= 1e-5 * sum|a b| + 1e-6, while the GEMM meets it.  Page
 "Fine-Grained FP8/FP4 Quantization", section "Hopper: CUDA Core Promotion (Nc=128)": the FP8
 tensor-core sum is kept at reduced precision, which the method contains by promoting every
@@ -14,6 +14,7 @@ import pytest
 import torch
 
 import fine_grained_block_fgq_amd as fgq
+from fine_grained_block_fgq_amd import calib
 import oracle
 import synth
 from tests.gpu_util import dev_u8, gemm_error_ratio, gpu_gemm, log
@@ -22,7 +23,7 @@ pytestmark = pytest.mark.gpu
 
 
 def probe(Aq, Bq):
-    P = fgq.fgq_probe_fp8_mfma_partials(dev_u8(Aq), dev_u8(Bq))
+    P = calib.fgq_probe_fp8_mfma_partials(dev_u8(Aq), dev_u8(Bq))
     torch.cuda.synchronize()
     return P.cpu().numpy().astype(np.float64)
 
@@ -55,7 +56,7 @@ def test_probe_layout_exact_on_unit_codes():
 def test_probe_shape_checks():
     log("fp8 mfma probe M=8 (not a multiple of 16)")
     with pytest.raises(fgq.FgqError) as e:
-        fgq.fgq_probe_fp8_mfma_partials(torch.zeros((8, 128), dtype=torch.uint8, device="cuda"),
+        calib.fgq_probe_fp8_mfma_partials(torch.zeros((8, 128), dtype=torch.uint8, device="cuda"),
                                         torch.zeros((128, 16), dtype=torch.uint8, device="cuda"))
     assert e.value.status == -2
 
@@ -96,11 +97,11 @@ def test_fp8_mfma_sum_misses_the_tolerance_the_gemm_meets():
 def test_calib_mfma_fp8_runs_and_repeats():
     log("calib_mfma_fp8 blocks=8 iters=5")
     out = torch.zeros((8 * 512,), dtype=torch.float32, device="cuda")
-    flops = fgq.fgq_calib_mfma_fp8(out, 8, 5)
+    flops = calib.fgq_calib_mfma_fp8(out, 8, 5)
     torch.cuda.synchronize()
     assert flops == 8 * 8 * 5 * 16 * 65536
     first = out.clone()
-    fgq.fgq_calib_mfma_fp8(out, 8, 5)
+    calib.fgq_calib_mfma_fp8(out, 8, 5)
     torch.cuda.synchronize()
     assert torch.isfinite(first).all()
     assert torch.equal(first, out)

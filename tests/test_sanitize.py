@@ -3,7 +3,8 @@
 * The oracle (oracle/fgq_oracle.c): every entry point on small seeded inputs spanning the
   bf16 exponent range, all-zero groups, and refused shapes
   (tests/helpers/oracle_sanitize_main.c).
-* The C ABI layer (fine_grained_block_fgq_amd/csrc/api.cpp) linked against stub launchers:
+* The C ABI layers (fine_grained_block_fgq_amd/csrc/api.cpp and calib_api.cpp, the
+  measurement library's) linked against stub launchers:
   every entry point with valid arguments reaches its launcher once and maps the launcher's
   status (success, launch failure, a grid too large for one dispatch); invalid or empty
   arguments never reach a launcher (tests/helpers/abi_stub_main.cpp).
@@ -51,6 +52,8 @@ def test_abi_layer_with_stub_launchers_under_sanitizers(tmp_path):
     out = _build_and_run(["g++", "-std=c++17", "-D__HIP_PLATFORM_AMD__", "-I", hip_include,
                           "-I", os.path.join(ROOT, "fine_grained_block_fgq_amd", "csrc"), *SAN,
                           os.path.join(ROOT, "fine_grained_block_fgq_amd", "csrc", "api.cpp"),
+                          os.path.join(ROOT, "fine_grained_block_fgq_amd", "csrc",
+                                       "calib_api.cpp"),
                           os.path.join(HELPERS, "abi_stub_main.cpp")],
                          "abi_san", tmp_path)
     assert out.strip() == "ok"
