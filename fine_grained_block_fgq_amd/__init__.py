@@ -58,6 +58,13 @@ def load() -> ctypes.CDLL:
     lib.fgq_gemm_fp8_blockscaled.argtypes = [p, p, p, p, p, i64, i64, i64, i32, p]
     lib.fgq_gemm_fp8_blockscaled_variant.restype = i32
     lib.fgq_gemm_fp8_blockscaled_variant.argtypes = [p, p, p, p, p, i64, i64, i64, i32, i32, p]
+    lib.fgq_gemm_workspace_size.restype = i64
+    lib.fgq_gemm_workspace_size.argtypes = [i64, i64, i64]
+    lib.fgq_gemm_fp8_blockscaled_ws.restype = i32
+    lib.fgq_gemm_fp8_blockscaled_ws.argtypes = [p, p, p, p, p, i64, i64, i64, i32, p, i64, p]
+    lib.fgq_gemm_fp8_blockscaled_splitk.restype = i32
+    lib.fgq_gemm_fp8_blockscaled_splitk.argtypes = [p, p, p, p, p, i64, i64, i64, i32, i32, p,
+                                                    i64, p]
     lib.fgq_quantize_act_1x128_ue8m0.restype = i32
     lib.fgq_quantize_act_1x128_ue8m0.argtypes = [p, p, p, i64, i64, p]
     lib.fgq_quantize_weight_128x128_ue8m0.restype = i32
@@ -153,7 +160,43 @@ def fgq_gemm_fp8_blockscaled_variant(A_q: torch.Tensor, scale_A: torch.Tensor,
                  variant, stream)
 
 
-def _gemm(fn, A_q, scale_A, B_q, scale_B, C, out_dtype, variant, stream):
+def fgq_gemm_workspace_size(M: int, N: int, K: int) -> int:
+    """Bytes of workspace fgq_gemm_fp8_blockscaled_ws splits K with for this shape on the
+    current device (0: none needed)."""
+    n = load().fgq_gemm_workspace_size(M, N, K)
+    if n < 0:
+        _check("fgq_gemm_workspace_size", int(n))
+    return int(n)
+
+
+def _workspace(ws):
+    if ws is None:
+        return None, 0
+    if not isinstance(ws, torch.Tensor) or not ws.is_cuda or not ws.is_contiguous():
+        raise TypeError("workspace must be a contiguous CUDA (ROCm) tensor")
+    return ws.data_ptr(), ws.numel() * ws.element_size()
+
+
+def fgq_gemm_fp8_blockscaled_ws(A_q: torch.Tensor, scale_A: torch.Tensor, B_q: torch.Tensor,
+                                scale_B: torch.Tensor, workspace: torch.Tensor | None,
+                                C: torch.Tensor | None = None,
+                                out_dtype: torch.dtype = torch.bfloat16, stream=None):
+    """fgq_gemm_fp8_blockscaled with a caller-owned workspace (any dtype, contiguous device
+    tensor of at least fgq_gemm_workspace_size bytes) for the K split of few-tile shapes."""
+    return _gemm("fgq_gemm_fp8_blockscaled_ws", A_q, scale_A, B_q, scale_B, C, out_dtype, None,
+                 stream, tail=list(_workspace(workspace)))
+
+
+def fgq_gemm_fp8_blockscaled_splitk(A_q: torch.Tensor, scale_A: torch.Tensor,
+                                    B_q: torch.Tensor, scale_B: torch.Tensor, splits: int,
+                                    workspace: torch.Tensor | None, C: torch.Tensor | None = None,
+                                    out_dtype: torch.dtype = torch.bfloat16, stream=None):
+    """The K-split GEMM with an explicit split count (workspace >= splits*M*N*4 bytes)."""
+    return _gemm("fgq_gemm_fp8_blockscaled_splitk", A_q, scale_A, B_q, scale_B, C, out_dtype,
+                 int(splits), stream, tail=list(_workspace(workspace)))
+
+
+def _gemm(fn, A_q, scale_A, B_q, scale_B, C, out_dtype, variant, stream, tail=()):
     lib = load()
     M, K = A_q.shape
     K2, N = B_q.shape
@@ -171,7 +214,7 @@ def _gemm(fn, A_q, scale_A, B_q, scale_B, C, out_dtype, variant, stream):
             _dev(C, "C", C.dtype, (M, N)), M, N, K, code]
     if variant is not None:
         args.append(int(variant))
-    _check(fn, getattr(lib, fn)(*args, _stream(stream)))
+    _check(fn, getattr(lib, fn)(*args, *tail, _stream(stream)))
     return C
 
 

@@ -83,6 +83,33 @@ int check_gemm(const void* A_q, const void* scale_A, const void* B_q, const void
     return FGQ_OK;
 }
 
+// the workspace of a K-split GEMM: splits * M * N floats that overlap no operand
+int check_workspace(const void* A_q, const void* scale_A, const void* B_q, const void* scale_B,
+                    const void* C, int64_t M, int64_t N, int64_t K, int out_dtype,
+                    const void* ws, int64_t ws_bytes, int64_t need)
+{
+    if (ws_bytes < 0)
+        return FGQ_ERR_SHAPE;
+    if (need > 0 && (!ws || ws_bytes < need))
+        return FGQ_ERR_WORKSPACE;
+    if (need <= 0)
+        return FGQ_OK;
+    if (misaligned(ws))
+        return FGQ_ERR_ALIGN;
+    const int64_t nc = M * N * (out_dtype == FGQ_OUT_BF16 ? 2 : 4);
+    if (overlap(ws, need, C, nc) || overlap(ws, need, A_q, M * K) ||
+        overlap(ws, need, B_q, K * N) || overlap(ws, need, scale_A, 4 * M * (K / 128)) ||
+        overlap(ws, need, scale_B, 4 * (K / 128) * (N / 128)))
+        return FGQ_ERR_ALIAS;
+    return FGQ_OK;
+}
+
+// bytes of the K-split workspace for `splits` splits (0 for none)
+int64_t split_bytes(int64_t M, int64_t N, int splits)
+{
+    return splits > 1 ? (int64_t)splits * M * N * 4 : 0;
+}
+
 }  // namespace
 
 extern "C" {
@@ -100,6 +127,7 @@ const char* fgq_status_string(int status)
     case FGQ_ERR_LAUNCH: return "kernel launch failed";
     case FGQ_ERR_ALIAS: return "output overlaps another buffer";
     case FGQ_ERR_VARIANT: return "unknown GEMM variant";
+    case FGQ_ERR_WORKSPACE: return "workspace too small for the call";
     default: return "unknown status";
     }
 }
@@ -154,6 +182,62 @@ int fgq_gemm_fp8_blockscaled_variant(const void* A_q, const float* scale_A, cons
     return launch_status(fgq::launch_gemm_fp8_blockscaled(A_q, scale_A, B_q, scale_B, C, M, N, K,
                                                           out_dtype == FGQ_OUT_BF16, variant,
                                                           static_cast<hipStream_t>(stream)));
+}
+
+int64_t fgq_gemm_workspace_size(int64_t M, int64_t N, int64_t K)
+{
+    if (M < 0 || N < 0 || K < 0 || K % 128 != 0 || N % 128 != 0 || M > kMaxDim ||
+        N > kMaxDim || K > kMaxDim || ((M + 127) / 128) * (N / 128) > kMaxDim)
+        return FGQ_ERR_SHAPE;
+    if (M == 0 || N == 0 || K == 0)
+        return 0;
+    return split_bytes(M, N, fgq::gemm_splitk_plan(M, N, K));
+}
+
+int fgq_gemm_fp8_blockscaled_splitk(const void* A_q, const float* scale_A, const void* B_q,
+                                    const float* scale_B, void* C, int64_t M, int64_t N,
+                                    int64_t K, int out_dtype, int splits, void* workspace,
+                                    int64_t workspace_bytes, void* stream)
+{
+    int st = check_gemm(A_q, scale_A, B_q, scale_B, C, M, N, K, out_dtype, FGQ_GEMM_AUTO, 4);
+    if (st != FGQ_OK)
+        return st;
+    if (splits < 1 || splits > fgq::kSplitMax || (K > 0 && splits > K / 128))
+        return FGQ_ERR_SHAPE;
+    if (M == 0 || N == 0)
+        return FGQ_OK;
+    if (K == 0)
+        splits = 1;
+    st = check_workspace(A_q, scale_A, B_q, scale_B, C, M, N, K, out_dtype, workspace,
+                         workspace_bytes, split_bytes(M, N, splits));
+    if (st != FGQ_OK)
+        return st;
+    return launch_status(fgq::launch_gemm_fp8_blockscaled_splitk(
+        A_q, scale_A, B_q, scale_B, C, M, N, K, out_dtype == FGQ_OUT_BF16, splits,
+        static_cast<float*>(workspace), static_cast<hipStream_t>(stream)));
+}
+
+int fgq_gemm_fp8_blockscaled_ws(const void* A_q, const float* scale_A, const void* B_q,
+                                const float* scale_B, void* C, int64_t M, int64_t N, int64_t K,
+                                int out_dtype, void* workspace, int64_t workspace_bytes,
+                                void* stream)
+{
+    int st = check_gemm(A_q, scale_A, B_q, scale_B, C, M, N, K, out_dtype, FGQ_GEMM_AUTO, 4);
+    if (st != FGQ_OK || M == 0 || N == 0)
+        return st;
+    if (workspace_bytes < 0)
+        return FGQ_ERR_SHAPE;
+    // the K split when the workspace holds its partials, else the no-workspace choice
+    int splits = K > 0 ? fgq::gemm_splitk_plan(M, N, K) : 1;
+    if (!workspace || workspace_bytes < split_bytes(M, N, splits))
+        splits = 1;
+    st = check_workspace(A_q, scale_A, B_q, scale_B, C, M, N, K, out_dtype, workspace,
+                         workspace_bytes, split_bytes(M, N, splits));
+    if (st != FGQ_OK)
+        return st;
+    return launch_status(fgq::launch_gemm_fp8_blockscaled_splitk(
+        A_q, scale_A, B_q, scale_B, C, M, N, K, out_dtype == FGQ_OUT_BF16, splits,
+        static_cast<float*>(workspace), static_cast<hipStream_t>(stream)));
 }
 
 int fgq_gemm_fp8_blockscaled_ue8m0(const void* A_q, const uint8_t* scale_A, const void* B_q,

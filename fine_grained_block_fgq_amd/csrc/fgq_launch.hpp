@@ -48,6 +48,16 @@ hipError_t launch_gemm_fp8_blockscaled_ue8m0(const void* A_q, const uint8_t* sA,
                                              int64_t M, int64_t N, int64_t K, int out_bf16,
                                              int variant, hipStream_t stream);
 
+// K split across workgroups with fp32 partials in a caller's workspace of
+// splits * M * N floats (splits <= 1: the automatic no-workspace choice); the number of
+// splits the workspace path uses for a shape on the current device (1 = none)
+constexpr int kSplitMax = 16;
+int gemm_splitk_plan(int64_t M, int64_t N, int64_t K);
+hipError_t launch_gemm_fp8_blockscaled_splitk(const void* A_q, const float* sA, const void* B_q,
+                                              const float* sB, void* C, int64_t M, int64_t N,
+                                              int64_t K, int out_bf16, int splits, float* ws,
+                                              hipStream_t stream);
+
 // C = bf16 GEMM result, plus its 1x128 E4M3 quantization (Cq [M,N], sC [M,N/128])
 hipError_t launch_gemm_fp8_blockscaled_quant(const void* A_q, const float* sA, const void* B_q,
                                              const float* sB, void* C, void* Cq, float* sC,

@@ -664,13 +664,19 @@ static hipError_t launch_cfg(const void* A_q, const void* sA_, const void* B_q, 
 // kernel's per-chunk code, so KG waves share each SIMD (latency hiding) while the A/B
 // stages stay within LDS.  The KG partial tiles are summed in LDS in group order (fixed:
 // results are repeatable bit for bit) and stored by group 0.
-template <class Cfg, class SI, bool OUT_BF16, int KG>
+//
+// With splits > 1 (PARTIAL) the K chunks are also divided between workgroups: the grid is
+// splits x tiles, workgroup (sp, tile) takes the consecutive chunks [sp*KB/splits,
+// (sp+1)*KB/splits) and writes its fp32 partial tile to the workspace slice sp (an [M, N]
+// array); splitk_reduce_kernel then sums the slices in slice order.
+template <class Cfg, class SI, bool OUT_BF16, int KG, bool PARTIAL = false>
 __global__ __launch_bounds__(Cfg::NT * KG) void gemm_fp8_blockscaled_ksplit_kernel(
     const uint8_t* __restrict__ A, const typename SI::T* __restrict__ sA,
     const uint8_t* __restrict__ B, const typename SI::T* __restrict__ sB,
-    void* __restrict__ Cout, int64_t M, int64_t N, int64_t K)
+    void* __restrict__ Cout, int64_t M, int64_t N, int64_t K, int64_t splits = 1)
 {
     static_assert(Cfg::WN * Cfg::TN == Cfg::BN && Cfg::BN <= 128, "skinny tile");
+    static_assert(!(PARTIAL && OUT_BF16), "partials are fp32");
     constexpr int RING = Cfg::STAGES * KG * Cfg::STAGE;
     constexpr int RED = (KG - 1) * Cfg::NT * Cfg::FM * Cfg::FN * 16;
     __shared__ __attribute__((aligned(1024))) uint8_t smem_raw[RING > RED ? RING : RED];
@@ -682,14 +688,20 @@ __global__ __launch_bounds__(Cfg::NT * KG) void gemm_fp8_blockscaled_ksplit_kern
     const int wm = wl / Cfg::WN, wn = wl % Cfg::WN;
     const int g = lane >> 4, q = lane & 15;
 
-    // tiles: row tiles fastest; XCD-contiguous ranges (ids are dealt round-robin to XCDs)
+    // tiles: row tiles fastest, then column tiles, then K splits; XCD-contiguous ranges (ids
+    // are dealt round-robin to XCDs), so the workgroups of one XCD share A's K range
     const int64_t tiles_m = (M + Cfg::BM - 1) / Cfg::BM;
+    const int64_t tiles = tiles_m * (N / Cfg::BN);
     const int64_t G = (int64_t)gridDim.x;
     int64_t pid = blockIdx.x;
     if (G % 8 == 0)
         pid = (pid % 8) * (G / 8) + pid / 8;
-    const int64_t m0 = (pid % tiles_m) * Cfg::BM, n0 = (pid / tiles_m) * Cfg::BN;
-    const int64_t KB = K / 128, NB = N / 128;
+    const int64_t sp = pid / tiles, tile = pid % tiles;
+    const int64_t m0 = (tile % tiles_m) * Cfg::BM, n0 = (tile / tiles_m) * Cfg::BN;
+    const int64_t KB_ALL = K / 128, NB = N / 128;
+    // this workgroup's chunks kb0 .. kb0+KB-1 (all of them without a split)
+    const int64_t kb0 = sp * KB_ALL / splits;
+    const int64_t KB = (sp + 1) * KB_ALL / splits - kb0;
     const int64_t steps = (KB + KG - 1) / KG;
 
     const FragOffsets<Cfg> fo(wm * Cfg::TM, wn * Cfg::FN, g, q);
@@ -704,35 +716,47 @@ __global__ __launch_bounds__(Cfg::NT * KG) void gemm_fp8_blockscaled_ksplit_kern
             acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
     // this group's chunk of step s is kb = s*KG + kg (if < KB)
-    ScaleBWalk<SI> sbw(sB + kg * NB + nb, KG * NB, kg < KB ? (KB - kg + KG - 1) / KG : 0, lane);
-    const ScaleBFlag<SI> sbf(sB + kg * NB + nb, KG * NB, kg < KB ? (KB - kg + KG - 1) / KG : 0,
-                             lane);
+    ScaleBWalk<SI> sbw(sB + (kb0 + kg) * NB + nb, KG * NB, kg < KB ? (KB - kg + KG - 1) / KG : 0,
+                       lane);
+    const ScaleBFlag<SI> sbf(sB + (kb0 + kg) * NB + nb, KG * NB,
+                             kg < KB ? (KB - kg + KG - 1) / KG : 0, lane);
     auto stage_of = [&](int64_t st) { return smem + ((st % Cfg::STAGES) * KG + kg) * Cfg::STAGE; };
+    // this group has a chunk in step c (its loads are issued only then)
+    auto has_chunk = [&](int64_t c) { return c < steps && c * KG + kg < KB; };
+    // every slot of the ring filled at once: with steps <= STAGES (the K range of a split
+    // workgroup) all of the workgroup's operands are requested before the first wait
 #pragma unroll
-    for (int st = 0; st < Cfg::STAGES - 1; ++st)
-        if (st < steps && st * KG + kg < KB)
-            load_stage<Cfg, SI>(stage_of(st), A, sA, B, M, N, K, m0, n0, st * KG + kg, wl, lane);
+    for (int st = 0; st < Cfg::STAGES; ++st)
+        if (has_chunk(st))
+            load_stage<Cfg, SI>(stage_of(st), A, sA, B, M, N, K, m0, n0, kb0 + st * KG + kg, wl,
+                                lane);
 
     auto k_loop = [&](auto big_tag) {
         constexpr bool BIG = decltype(big_tag)::value;
         for (int64_t st = 0; st < steps; ++st) {
             const int64_t kb = st * KG + kg;
-            // this wave's own loads issued for later steps (chunk present in those steps)
+            // this wave's loads of later steps already issued (the prologue's, then one step
+            // per iteration): step st has landed once only those may be outstanding
             int later = 0;
-    #pragma unroll
-            for (int d = 1; d <= Cfg::STAGES - 2; ++d)
-                later += (st + d < steps && (st + d) * KG + kg < KB) ? 1 : 0;
-            if (Cfg::STAGES >= 4 && later >= 2)
+#pragma unroll
+            for (int d = 1; d < Cfg::STAGES; ++d) {
+                const int64_t c = st + d;
+                const bool issued = c < Cfg::STAGES || c <= st + Cfg::STAGES - 2;
+                later += (issued && has_chunk(c)) ? 1 : 0;
+            }
+            if (later >= 3)
+                wait_vm<3 * Cfg::MIN_LOADS>();
+            else if (later == 2)
                 wait_vm<2 * Cfg::MIN_LOADS>();
-            else if (Cfg::STAGES >= 3 && later >= 1)
+            else if (later == 1)
                 wait_vm<Cfg::MIN_LOADS>();
             else
                 wait_vm<0>();
-            lds_barrier();   // step st visible to all; step st-1 fully read (its stage refills)
-            const int64_t nxt = st + Cfg::STAGES - 1;
-            if (nxt < steps && nxt * KG + kg < KB)
-                load_stage<Cfg, SI>(stage_of(nxt), A, sA, B, M, N, K, m0, n0, nxt * KG + kg, wl,
-                                    lane);
+            lds_barrier();   // step st visible to all; step st-1 fully read (its slot refills)
+            const int64_t nxt = st - 1 + Cfg::STAGES;
+            if (st >= 1 && has_chunk(nxt))
+                load_stage<Cfg, SI>(stage_of(nxt), A, sA, B, M, N, K, m0, n0,
+                                    kb0 + nxt * KG + kg, wl, lane);
             if (kb < KB) {
                 const float sb = sbw.get(st);
                 compute_chunk<Cfg, SI, BIG>(stage_of(st), fo, s_off, sb, acc);
@@ -770,7 +794,8 @@ __global__ __launch_bounds__(Cfg::NT * KG) void gemm_fp8_blockscaled_ksplit_kern
                 acc[i][j] += *(const f32x4 LDS*)(red + (((c - 1) * Cfg::NT + wl * 64 + lane) *
                                                             PER_LANE +
                                                         (i * Cfg::FN + j) * 4));
-    // lane holds C[16i + 4g + r][16j + q] of the wave tile
+    // lane holds C[16i + 4g + r][16j + q] of the wave tile (or, split, the partial of it)
+    float* const P = PARTIAL ? static_cast<float*>(Cout) + sp * M * N : nullptr;
 #pragma unroll
     for (int i = 0; i < Cfg::FM; ++i)
 #pragma unroll
@@ -781,7 +806,9 @@ __global__ __launch_bounds__(Cfg::NT * KG) void gemm_fp8_blockscaled_ksplit_kern
 #pragma unroll
             for (int j = 0; j < Cfg::FN; ++j) {
                 const int64_t col = n0 + wn * Cfg::TN + 16 * j + q;
-                if (OUT_BF16)
+                if (PARTIAL)
+                    P[row * N + col] = acc[i][j][r];
+                else if (OUT_BF16)
                     static_cast<__bf16*>(Cout)[row * N + col] = (__bf16)acc[i][j][r];
                 else
                     static_cast<float*>(Cout)[row * N + col] = acc[i][j][r];
@@ -1181,6 +1208,119 @@ hipError_t launch_gemm_fp8_blockscaled_quant(const void* A_q, const float* sA, c
     if (M >= 256 && tiles_large >= 256)
         return launch_fused<CfgLarge>(A_q, sA, B_q, sB, C, Cq, sC, M, N, K, stream);
     return launch_fused<CfgSmall>(A_q, sA, B_q, sB, C, Cq, sC, M, N, K, stream);
+}
+
+// ---------------------------------------------------------------------------------------
+// K split across workgroups (stream-K style, for shapes with few output tiles such as the
+// decode-like M <= 128).  Pass 1 runs splits x tiles workgroups of the K-group kernel with
+// 128x128 tiles (8 waves: a 2x2 grid of 64x64 wave tiles in each of two K groups), each over a
+// contiguous range of K chunks, writing fp32 partial tiles to the workspace slices [splits][M][N];
+// pass 2 sums the slices in slice order ((p0 + p1) + p2) + ..., so results are repeatable bit
+// for bit, and writes C.  No atomics: every workspace element is written by exactly one
+// workgroup of pass 1 and read by pass 2, which the stream orders after it.
+using CfgSplit = GemmCfg<128, 128, 2, 2, 2>;
+constexpr int SPLIT_KG = 2;
+constexpr int SPLIT_MAX = kSplitMax;
+
+// sum of the partial slices, 8 consecutive elements per thread (M*N is a multiple of 128):
+// all slices' loads are issued before the first add, then added in slice order
+template <bool OUT_BF16, int S>
+__global__ __launch_bounds__(256) void splitk_reduce_kernel(const float* __restrict__ P,
+                                                            void* __restrict__ C, int64_t MN)
+{
+    const int64_t i = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 8;
+    if (i >= MN)
+        return;
+    f32x4 part[S][2];
+#pragma unroll
+    for (int sp = 0; sp < S; ++sp) {
+        part[sp][0] = __builtin_nontemporal_load((const f32x4*)(P + sp * MN + i));
+        part[sp][1] = __builtin_nontemporal_load((const f32x4*)(P + sp * MN + i + 4));
+    }
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+        f32x4 v = part[0][h];
+#pragma unroll
+        for (int sp = 1; sp < S; ++sp)
+            v += part[sp][h];
+        if (OUT_BF16) {
+            typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+            *(bf16x4*)(static_cast<__bf16*>(C) + i + 4 * h) =
+                bf16x4{(__bf16)v[0], (__bf16)v[1], (__bf16)v[2], (__bf16)v[3]};
+        } else {
+            *(f32x4*)(static_cast<float*>(C) + i + 4 * h) = v;
+        }
+    }
+}
+
+template <bool OUT_BF16, int S = 2>
+static void launch_reduce(const float* ws, void* C, int64_t MN, int splits, int64_t blocks,
+                          hipStream_t stream)
+{
+    if constexpr (S < SPLIT_MAX) {
+        if (splits != S)
+            return launch_reduce<OUT_BF16, S + 1>(ws, C, MN, splits, blocks, stream);
+    }
+    hipLaunchKernelGGL((splitk_reduce_kernel<OUT_BF16, S>), dim3((unsigned)blocks), dim3(256), 0,
+                       stream, ws, C, MN);
+}
+
+// K splits the workspace path uses for a shape (1 = none).  Two launches cost ~8 us of fixed
+// time more than one on this GPU (measured: the reduction pass alone adds 8 us at
+// 128x7168x2048), so the split pays only where the unsplit kernels would walk long K chains
+// on few workgroups: 128 or more K chunks with 128x128 tiles covering at most half of the
+// CUs (back to back: 128x512x32768 72 -> 29 us, 128x1024x16384 31 -> 23 us,
+// 512x1024x16384 39 -> 33 us; with 32-64 chunks the unsplit kernels were as fast or faster).
+// Then the largest power of two (<= SPLIT_MAX) whose workgroups fit one round of the CUs with
+// at least 8 chunks each.
+int gemm_splitk_plan(int64_t M, int64_t N, int64_t K)
+{
+    const int cus = device_cus() > 0 ? device_cus() : 256;
+    const int64_t tiles = ((M + 127) / 128) * (N / 128), KB = K / 128;
+    if (tiles <= 0 || 2 * tiles > cus || KB < 128)
+        return 1;
+    int sp = 1;
+    while (2 * sp <= SPLIT_MAX && tiles * 2 * sp <= cus && KB / (2 * sp) >= 8)
+        sp *= 2;
+    return sp;
+}
+
+template <class SI>
+static hipError_t launch_splitk(const void* A_q, const void* sA_, const void* B_q,
+                                const void* sB_, void* C, int64_t M, int64_t N, int64_t K,
+                                int out_bf16, int splits, float* ws, hipStream_t stream)
+{
+    const typename SI::T* sA = static_cast<const typename SI::T*>(sA_);
+    const typename SI::T* sB = static_cast<const typename SI::T*>(sB_);
+    const int64_t tiles = ((M + CfgSplit::BM - 1) / CfgSplit::BM) * (N / CfgSplit::BN);
+    const int64_t MN = M * N;
+    const int64_t rblocks = (MN / 8 + 255) / 256;
+    if (!grid_fits(tiles * splits, CfgSplit::NT * SPLIT_KG) || !grid_fits(rblocks, 256))
+        return hipErrorInvalidConfiguration;
+    hipLaunchKernelGGL((gemm_fp8_blockscaled_ksplit_kernel<CfgSplit, SI, false, SPLIT_KG, true>),
+                       dim3((unsigned)(tiles * splits)), dim3(CfgSplit::NT * SPLIT_KG), 0,
+                       stream, static_cast<const uint8_t*>(A_q), sA,
+                       static_cast<const uint8_t*>(B_q), sB, ws, M, N, K, (int64_t)splits);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess)
+        return e;
+    if (out_bf16)
+        launch_reduce<true>(ws, C, MN, splits, rblocks, stream);
+    else
+        launch_reduce<false>(ws, C, MN, splits, rblocks, stream);
+    return hipGetLastError();
+}
+
+hipError_t launch_gemm_fp8_blockscaled_splitk(const void* A_q, const float* sA, const void* B_q,
+                                              const float* sB, void* C, int64_t M, int64_t N,
+                                              int64_t K, int out_bf16, int splits, float* ws,
+                                              hipStream_t stream)
+{
+    if (splits <= 1)
+        return launch_gemm<ScaleIn<false>>(A_q, sA, B_q, sB, C, M, N, K, out_bf16, GEMM_AUTO,
+                                           stream);
+    return launch_splitk<ScaleIn<false>>(A_q, sA, B_q, sB, C, M, N, K, out_bf16, splits, ws,
+                                         stream);
 }
 
 }  // namespace fgq

@@ -46,7 +46,8 @@ typedef enum {
     FGQ_ERR_DTYPE = -4,  /* unknown out_dtype */
     FGQ_ERR_LAUNCH = -5, /* the HIP launch failed (hipGetLastError) */
     FGQ_ERR_ALIAS = -6,  /* an output overlaps an input or another output */
-    FGQ_ERR_VARIANT = -7 /* unknown GEMM kernel variant */
+    FGQ_ERR_VARIANT = -7, /* unknown GEMM kernel variant */
+    FGQ_ERR_WORKSPACE = -8 /* a workspace is missing or smaller than the call needs */
 } fgq_status;
 
 typedef enum { FGQ_OUT_F32 = 0, FGQ_OUT_BF16 = 1 } fgq_out_dtype;
@@ -123,6 +124,46 @@ typedef enum {
 int fgq_gemm_fp8_blockscaled_variant(const void* A_q, const float* scale_A, const void* B_q,
                                      const float* scale_B, void* C, int64_t M, int64_t N,
                                      int64_t K, int out_dtype, int variant, void* stream);
+
+/*
+ * The same GEMM with the K chunks also divided between workgroups (a stream-K style split;
+ * page "Persistent kernel (grid = SM count, internal tile loop)", section "Variants": one
+ * tile's K loop spread over several workgroups), for shapes whose output tiles are too few to
+ * occupy the GPU (decode-like M <= 128: 128x7168 has 56 tiles of 128x128 for 256 CUs).
+ * Workgroup (s, tile) forms the fp32 partial of its tile over the consecutive K chunks
+ * [s*KB/splits, (s+1)*KB/splits), KB = K/128, into slice s of a caller-owned workspace
+ * (fp32 [splits][M][N], splits*M*N*4 bytes); a second kernel on the same stream sums the slices
+ * in slice order and writes C.  Every workspace element is written once and read once: no
+ * atomics, and a given shape and split count always gives the same bits.  The sum differs
+ * from the unsplit kernels' by fp32 rounding only (same tolerance).
+ *
+ * fgq_gemm_workspace_size: bytes fgq_gemm_fp8_blockscaled_ws needs for this shape on the
+ *   current device (0: the shape runs unsplit and needs none); a negative fgq_status for an
+ *   invalid shape.  The split count it plans: 1 (no workspace) unless K/128 >= 128 and the
+ *   128x128 output tiles cover at most half of the GPU's CUs -- the second launch costs
+ *   more than the split gains on shorter K -- else the largest power of two up to 16 whose
+ *   workgroups fit one round of the CUs with at least 8 K chunks each.
+ * fgq_gemm_fp8_blockscaled_ws: fgq_gemm_fp8_blockscaled with a workspace; it splits K as
+ *   planned when workspace_bytes >= fgq_gemm_workspace_size(M, N, K), and otherwise (also
+ *   with workspace == NULL) computes C exactly as fgq_gemm_fp8_blockscaled does, using no
+ *   workspace.  The workspace is device memory owned by the caller, 16-byte aligned, not
+ *   overlapping any operand; its contents on entry are irrelevant and on return undefined;
+ *   calls that share a workspace must not overlap in time.
+ * fgq_gemm_fp8_blockscaled_splitk: the same with an explicit split count (tests, tuning):
+ *   1 <= splits <= 16 and splits <= K/128 (FGQ_ERR_SHAPE otherwise); splits == 1 is the
+ *   unsplit choice; splits > 1 needs workspace_bytes >= splits*M*N*4 (FGQ_ERR_WORKSPACE).
+ * Other arguments, requirements and errors as fgq_gemm_fp8_blockscaled; FGQ_ERR_ALIAS when
+ * the workspace overlaps an operand.
+ */
+int64_t fgq_gemm_workspace_size(int64_t M, int64_t N, int64_t K);
+int fgq_gemm_fp8_blockscaled_ws(const void* A_q, const float* scale_A, const void* B_q,
+                                const float* scale_B, void* C, int64_t M, int64_t N, int64_t K,
+                                int out_dtype, void* workspace, int64_t workspace_bytes,
+                                void* stream);
+int fgq_gemm_fp8_blockscaled_splitk(const void* A_q, const float* scale_A, const void* B_q,
+                                    const float* scale_B, void* C, int64_t M, int64_t N,
+                                    int64_t K, int out_dtype, int splits, void* workspace,
+                                    int64_t workspace_bytes, void* stream);
 
 /*
  * Block-scaled FP8 GEMM with the next layer's activation quantization fused into its

@@ -68,6 +68,14 @@ hipError_t launch_gemm_nvfp4(const void*, const uint8_t*, const float*, const vo
 {
     return stub();
 }
+hipError_t launch_gemm_fp8_blockscaled_splitk(const void*, const float*, const void*,
+                                              const float*, void*, int64_t, int64_t, int64_t, int,
+                                              int, float*, hipStream_t)
+{
+    return stub();
+}
+// the plan of the stubbed device: 4 splits for M <= 128, else none
+int gemm_splitk_plan(int64_t M, int64_t, int64_t K) { return M <= 128 && K >= 2048 ? 4 : 1; }
 hipError_t launch_calib_stream(const void*, void*, int64_t, hipStream_t) { return stub(); }
 hipError_t launch_calib_mfma_f16(float*, int64_t, int64_t, hipStream_t) { return stub(); }
 hipError_t launch_calib_mfma_fp8(float*, int64_t, int64_t, hipStream_t) { return stub(); }
@@ -125,6 +133,14 @@ void all_entry_points(int want)
     expect("gemm_nvfp4", fgq_gemm_nvfp4(at(1), uat(2), fat(3), at(4), uat(5), fat(6), at(7), 4,
                                         128, 256, FGQ_OUT_F32, nullptr),
            want, 1);
+    expect("gemm_ws", fgq_gemm_fp8_blockscaled_ws(at(1), fat(2), at(3), fat(4), at(5), 4, 128,
+                                                  2048, FGQ_OUT_F32, at(6), 4 * 4 * 128 * 4,
+                                                  nullptr),
+           want, 1);
+    expect("gemm_splitk", fgq_gemm_fp8_blockscaled_splitk(at(1), fat(2), at(3), fat(4), at(5),
+                                                          4, 128, 256, FGQ_OUT_BF16, 2, at(6),
+                                                          2 * 4 * 128 * 4, nullptr),
+           want, 1);
     expect("calib_stream", fgq_calib_stream(at(1), at(2), 100, nullptr), want, 1);
     expect("calib_mfma_f16", fgq_calib_mfma_f16(fat(1), 4, 10, nullptr), want, 1);
     expect("calib_mfma_fp8", fgq_calib_mfma_fp8(fat(1), 4, 10, nullptr), want, 1);
@@ -168,7 +184,34 @@ int main()
            FGQ_OK, 1);   // K == 0 still writes C = 0: the launcher runs
     expect("nvfp4 C%16", fgq_quantize_nvfp4(at(1), at(2), uat(3), fat(4), 4, 24, nullptr),
            FGQ_ERR_SHAPE, 0);
-    for (int s = 0; s >= -7; --s)
+    expect("splitk small workspace",
+           fgq_gemm_fp8_blockscaled_splitk(at(1), fat(2), at(3), fat(4), at(5), 4, 128, 256,
+                                           FGQ_OUT_F32, 2, at(6), 2 * 4 * 128 * 4 - 1, nullptr),
+           FGQ_ERR_WORKSPACE, 0);
+    expect("splitk no workspace",
+           fgq_gemm_fp8_blockscaled_splitk(at(1), fat(2), at(3), fat(4), at(5), 4, 128, 256,
+                                           FGQ_OUT_F32, 2, nullptr, 0, nullptr),
+           FGQ_ERR_WORKSPACE, 0);
+    expect("splitk splits > K/128",
+           fgq_gemm_fp8_blockscaled_splitk(at(1), fat(2), at(3), fat(4), at(5), 4, 128, 256,
+                                           FGQ_OUT_F32, 3, at(6), 1 << 20, nullptr),
+           FGQ_ERR_SHAPE, 0);
+    expect("splitk workspace alias",
+           fgq_gemm_fp8_blockscaled_splitk(at(1), fat(2), at(3), fat(4), at(5), 4, 128, 256,
+                                           FGQ_OUT_F32, 2, at(5), 1 << 20, nullptr),
+           FGQ_ERR_ALIAS, 0);
+    // the workspace path: too small a workspace falls back to the unsplit launch
+    expect("ws fallback", fgq_gemm_fp8_blockscaled_ws(at(1), fat(2), at(3), fat(4), at(5), 4,
+                                                      128, 2048, FGQ_OUT_F32, at(6), 16,
+                                                      nullptr),
+           FGQ_OK, 1);
+    if (fgq_gemm_workspace_size(4, 128, 2048) != 4 * 4 * 128 * 4 ||
+        fgq_gemm_workspace_size(256, 128, 2048) != 0 ||
+        fgq_gemm_workspace_size(4, 100, 2048) != FGQ_ERR_SHAPE) {
+        std::printf("FAIL workspace size\n");
+        ++failures;
+    }
+    for (int s = 0; s >= -8; --s)
         if (!fgq_status_string(s) || !fgq_status_string(s)[0]) {
             std::printf("FAIL status string %d\n", s);
             ++failures;

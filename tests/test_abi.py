@@ -48,7 +48,7 @@ def test_measurement_library_is_separate():
 
 def test_status_strings():
     lib = fgq.load()
-    for s in (0, -1, -2, -3, -4, -5, -6, -7):
+    for s in (0, -1, -2, -3, -4, -5, -6, -7, -8):
         assert lib.fgq_status_string(s)
     assert lib.fgq_status_string(-99) == b"unknown status"
 
@@ -56,6 +56,7 @@ def test_status_strings():
 P = 0x10000  # aligned fake addresses: validation fails before they could be used
 Q = 0x20000
 R = 0x30000
+T = 0x1000000
 
 
 @pytest.mark.parametrize("args,want", [
@@ -194,6 +195,42 @@ def test_nvfp4_validation(fn, args, want):
 ])
 def test_calib_validation(fn, args, want):
     assert getattr(calib.load(), fn)(*args, None) == want
+
+
+def test_workspace_size_validation():
+    lib = fgq.load()
+    assert lib.fgq_gemm_workspace_size(4, 100, 128) == -2      # N % 128
+    assert lib.fgq_gemm_workspace_size(4, 128, 100) == -2      # K % 128
+    assert lib.fgq_gemm_workspace_size(-1, 128, 128) == -2
+    assert lib.fgq_gemm_workspace_size(0, 128, 128) == 0       # empty: nothing to split
+    assert lib.fgq_gemm_workspace_size(4, 128, 0) == 0
+
+
+@pytest.mark.parametrize("args,want", [
+    ((P, S1, Q, S2, R, 4, 128, 256, 0, 0, T, 1 << 20), -2),    # splits < 1
+    ((P, S1, Q, S2, R, 4, 128, 256, 0, 3, T, 1 << 20), -2),    # splits > K/128
+    ((1 << 30, 2 << 30, 3 << 30, 4 << 30, 5 << 30, 4, 128, 4096, 0, 17, 6 << 30, 1 << 20),
+     -2),                                                      # splits > 16
+    ((P, S1, Q, S2, R, 4, 128, 256, 0, 2, T, 4095), -8),       # workspace < 2*4*128*4
+    ((P, S1, Q, S2, R, 4, 128, 256, 0, 2, None, 0), -8),
+    ((P, S1, Q, S2, R, 4, 128, 256, 0, 2, T + 8, 1 << 20), -3),
+    ((P, S1, Q, S2, R, 4, 128, 256, 0, 2, R, 1 << 20), -6),    # workspace overlaps C
+    ((P, S1, Q, S2, R, 4, 128, 256, 0, 2, T, -1), -2),
+])
+def test_splitk_validation(args, want):
+    assert fgq.load().fgq_gemm_fp8_blockscaled_splitk(*args, None) == want
+
+
+def test_ws_validation():
+    lib = fgq.load()
+    # dtype and shape errors as the plain GEMM; a negative workspace size is a shape error
+    assert lib.fgq_gemm_fp8_blockscaled_ws(P, S1, Q, S2, R, 4, 128, 256, 2, T, 1 << 20,
+                                           None) == -4
+    assert lib.fgq_gemm_fp8_blockscaled_ws(P, S1, Q, S2, R, 4, 100, 256, 0, T, 1 << 20,
+                                           None) == -2
+    assert lib.fgq_gemm_fp8_blockscaled_ws(P, S1, Q, S2, R, 4, 128, 256, 0, T, -5, None) == -2
+    assert lib.fgq_gemm_fp8_blockscaled_ws(None, None, None, None, None, 0, 128, 256, 0, None,
+                                           0, None) == 0
 
 
 # Shapes that pass the argument checks but whose grid would exceed the 2^32 work-items one
