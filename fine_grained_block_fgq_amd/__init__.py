@@ -65,6 +65,8 @@ def load() -> ctypes.CDLL:
     lib.fgq_gemm_fp8_blockscaled_splitk.restype = i32
     lib.fgq_gemm_fp8_blockscaled_splitk.argtypes = [p, p, p, p, p, i64, i64, i64, i32, i32, p,
                                                     i64, p]
+    lib.fgq_gemm_fp8_blockscaled_noalloc.restype = i32
+    lib.fgq_gemm_fp8_blockscaled_noalloc.argtypes = [p, p, p, p, p, i64, i64, i64, i32, p]
     lib.fgq_quantize_act_1x128_ue8m0.restype = i32
     lib.fgq_quantize_act_1x128_ue8m0.argtypes = [p, p, p, i64, i64, p]
     lib.fgq_quantize_weight_128x128_ue8m0.restype = i32
@@ -194,6 +196,16 @@ def fgq_gemm_fp8_blockscaled_splitk(A_q: torch.Tensor, scale_A: torch.Tensor,
     """The K-split GEMM with an explicit split count (workspace >= splits*M*N*4 bytes)."""
     return _gemm("fgq_gemm_fp8_blockscaled_splitk", A_q, scale_A, B_q, scale_B, C, out_dtype,
                  int(splits), stream, tail=list(_workspace(workspace)))
+
+
+def fgq_gemm_fp8_blockscaled_noalloc(A_q: torch.Tensor, scale_A: torch.Tensor,
+                                     B_q: torch.Tensor, scale_B: torch.Tensor,
+                                     C: torch.Tensor | None = None,
+                                     out_dtype: torch.dtype = torch.bfloat16, stream=None):
+    """fgq_gemm_fp8_blockscaled_ws with the library's own per-GPU array as its workspace (the C
+    entry point allocates nothing; pass C to keep the binding from allocating it)."""
+    return _gemm("fgq_gemm_fp8_blockscaled_noalloc", A_q, scale_A, B_q, scale_B, C, out_dtype,
+                 None, stream)
 
 
 def _gemm(fn, A_q, scale_A, B_q, scale_B, C, out_dtype, variant, stream, tail=()):

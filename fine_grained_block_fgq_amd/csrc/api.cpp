@@ -240,6 +240,22 @@ int fgq_gemm_fp8_blockscaled_ws(const void* A_q, const float* scale_A, const voi
         static_cast<float*>(workspace), static_cast<hipStream_t>(stream)));
 }
 
+int fgq_gemm_fp8_blockscaled_noalloc(const void* A_q, const float* scale_A, const void* B_q,
+                                     const float* scale_B, void* C, int64_t M, int64_t N,
+                                     int64_t K, int out_dtype, void* stream)
+{
+    const int st = check_gemm(A_q, scale_A, B_q, scale_B, C, M, N, K, out_dtype, FGQ_GEMM_AUTO,
+                              4);
+    if (st != FGQ_OK || M == 0 || N == 0)
+        return st;
+    const int splits = K > 0 ? fgq::gemm_splitk_plan(M, N, K) : 1;
+    if (split_bytes(M, N, splits) > fgq::kNoallocScratchBytes)
+        return FGQ_ERR_WORKSPACE;
+    return launch_status(fgq::launch_gemm_fp8_blockscaled_noalloc(
+        A_q, scale_A, B_q, scale_B, C, M, N, K, out_dtype == FGQ_OUT_BF16, splits,
+        static_cast<hipStream_t>(stream)));
+}
+
 int fgq_gemm_fp8_blockscaled_ue8m0(const void* A_q, const uint8_t* scale_A, const void* B_q,
                                    const uint8_t* scale_B, void* C, int64_t M, int64_t N,
                                    int64_t K, int out_dtype, int variant, void* stream)

@@ -58,6 +58,16 @@ hipError_t launch_gemm_fp8_blockscaled_splitk(const void* A_q, const float* sA, 
                                               int64_t K, int out_bf16, int splits, float* ws,
                                               hipStream_t stream);
 
+// the same K-split GEMM with its partials in a static per-device array of
+// kNoallocScratchBytes (no workspace argument, no allocation); splits * M * N * 4 beyond that
+// size is refused (hipErrorInvalidValue), a failed lookup of the array gives
+// hipErrorInvalidSymbol
+constexpr int64_t kNoallocScratchBytes = int64_t(16) << 20;
+hipError_t launch_gemm_fp8_blockscaled_noalloc(const void* A_q, const float* sA, const void* B_q,
+                                               const float* sB, void* C, int64_t M, int64_t N,
+                                               int64_t K, int out_bf16, int splits,
+                                               hipStream_t stream);
+
 // C = bf16 GEMM result, plus its 1x128 E4M3 quantization (Cq [M,N], sC [M,N/128])
 hipError_t launch_gemm_fp8_blockscaled_quant(const void* A_q, const float* sA, const void* B_q,
                                              const float* sB, void* C, void* Cq, float* sC,

@@ -1323,4 +1323,44 @@ hipError_t launch_gemm_fp8_blockscaled_splitk(const void* A_q, const float* sA, 
                                          stream);
 }
 
+// ---------------------------------------------------------------------------------------
+// For callers that cannot allocate (fgq_gemm_fp8_blockscaled_noalloc): the K-split partials
+// in a file-scope device array instead of a caller's workspace.  Every GPU the library runs
+// on holds its own copy (kNoallocScratchBytes) until the process ends; every call on a GPU
+// shares it, so calls that overlap in time on one GPU race.  Nothing in it has to start at
+// zero: pass 1 writes every partial element that pass 2 reads.
+static __device__ __align__(256) float scratch[kNoallocScratchBytes / 4];
+
+// the array's device address on the current GPU, looked up on the first call on each device
+// with that device current (the host-side name of a __device__ array is only a stand-in)
+static float* scratch_ptr()
+{
+    static std::atomic<float*> cache[64];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64)
+        return nullptr;
+    float* p = cache[dev].load(std::memory_order_acquire);
+    if (p)
+        return p;
+    void* q = nullptr;
+    if (hipGetSymbolAddress(&q, HIP_SYMBOL(scratch)) != hipSuccess || !q)
+        return nullptr;
+    cache[dev].store(static_cast<float*>(q), std::memory_order_release);
+    return static_cast<float*>(q);
+}
+
+hipError_t launch_gemm_fp8_blockscaled_noalloc(const void* A_q, const float* sA, const void* B_q,
+                                               const float* sB, void* C, int64_t M, int64_t N,
+                                               int64_t K, int out_bf16, int splits,
+                                               hipStream_t stream)
+{
+    if (splits > 1 && (int64_t)splits * M * N * 4 > kNoallocScratchBytes)
+        return hipErrorInvalidValue;
+    float* const ws = scratch_ptr();
+    if (!ws)
+        return hipErrorInvalidSymbol;
+    return launch_gemm_fp8_blockscaled_splitk(A_q, sA, B_q, sB, C, M, N, K, out_bf16, splits,
+                                              ws, stream);
+}
+
 }  // namespace fgq

@@ -166,6 +166,22 @@ int fgq_gemm_fp8_blockscaled_splitk(const void* A_q, const float* scale_A, const
                                     int64_t workspace_bytes, void* stream);
 
 /*
+ * fgq_gemm_fp8_blockscaled_ws for callers that cannot allocate device memory (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc): no workspace argument;
+ * the planned K split keeps its partials in a device array inside the library, 16 MiB per
+ * GPU, set up on the first call on each device and held until the process ends.  The call
+ * allocates nothing.  Every call on a GPU shares that GPU's array, so calls that overlap in
+ * time on one GPU (different streams, or threads) race and must be serialized by the
+ * caller.  Returns FGQ_ERR_WORKSPACE when the planned split would need more than 16 MiB
+ * (fgq_gemm_workspace_size(M, N, K) > 16 MiB; never on a GPU of up to 256 CUs, where the
+ * plan needs at most 16 MiB), FGQ_ERR_LAUNCH when the array cannot be located on the current
+ * device; otherwise arguments, results and errors as fgq_gemm_fp8_blockscaled_ws.
+ */
+int fgq_gemm_fp8_blockscaled_noalloc(const void* A_q, const float* scale_A, const void* B_q,
+                                     const float* scale_B, void* C, int64_t M, int64_t N,
+                                     int64_t K, int out_dtype, void* stream);
+
+/*
  * Block-scaled FP8 GEMM with the next layer's activation quantization fused into its
  * epilogue (page "Kernel Fusion": one launch instead of a round trip through memory):
  *   C       out: bf16 [M, N], the GEMM of fgq_gemm_fp8_blockscaled with FGQ_OUT_BF16

@@ -74,6 +74,12 @@ hipError_t launch_gemm_fp8_blockscaled_splitk(const void*, const float*, const v
 {
     return stub();
 }
+hipError_t launch_gemm_fp8_blockscaled_noalloc(const void*, const float*, const void*,
+                                               const float*, void*, int64_t, int64_t, int64_t,
+                                               int, int, hipStream_t)
+{
+    return stub();
+}
 // the plan of the stubbed device: 4 splits for M <= 128, else none
 int gemm_splitk_plan(int64_t M, int64_t, int64_t K) { return M <= 128 && K >= 2048 ? 4 : 1; }
 hipError_t launch_calib_stream(const void*, void*, int64_t, hipStream_t) { return stub(); }
@@ -140,6 +146,9 @@ void all_entry_points(int want)
     expect("gemm_splitk", fgq_gemm_fp8_blockscaled_splitk(at(1), fat(2), at(3), fat(4), at(5),
                                                           4, 128, 256, FGQ_OUT_BF16, 2, at(6),
                                                           2 * 4 * 128 * 4, nullptr),
+           want, 1);
+    expect("gemm_noalloc", fgq_gemm_fp8_blockscaled_noalloc(at(1), fat(2), at(3), fat(4), at(5),
+                                                            4, 128, 2048, FGQ_OUT_F32, nullptr),
            want, 1);
     expect("calib_stream", fgq_calib_stream(at(1), at(2), 100, nullptr), want, 1);
     expect("calib_mfma_f16", fgq_calib_mfma_f16(fat(1), 4, 10, nullptr), want, 1);
@@ -211,6 +220,11 @@ int main()
         std::printf("FAIL workspace size\n");
         ++failures;
     }
+    // the no-allocation GEMM refuses a planned split beyond its 16 MiB array
+    expect("noalloc too large", fgq_gemm_fp8_blockscaled_noalloc(at(1), fat(2), at(3), fat(4),
+                                                                 at(5), 128, 16384, 2048,
+                                                                 FGQ_OUT_F32, nullptr),
+           FGQ_ERR_WORKSPACE, 0);
     for (int s = 0; s >= -8; --s)
         if (!fgq_status_string(s) || !fgq_status_string(s)[0]) {
             std::printf("FAIL status string %d\n", s);
