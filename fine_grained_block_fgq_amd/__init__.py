@@ -28,6 +28,8 @@ _LIB_PATH = os.path.join(_HERE, "libfgq.so")
 FGQ_OUT_F32, FGQ_OUT_BF16 = 0, 1
 FGQ_GEMM_AUTO, FGQ_GEMM_WIDE_256x128, FGQ_GEMM_WIDE_128x128, FGQ_GEMM_NARROW_64x32 = 0, 1, 2, 3
 FGQ_GEMM_SKINNY_128x32, FGQ_GEMM_NARROW_64x64 = 4, 5
+# floats of the NVFP4 quantizer's global-scale argument (element 0 = the global scale)
+FGQ_NVFP4_GLOBAL_FLOATS = 512
 _lib = None
 
 
@@ -107,6 +109,16 @@ def _dev(t: torch.Tensor, name: str, dtype, shape):
         raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
     if not t.is_contiguous():
         raise ValueError(f"{name} must be contiguous")
+    return t.data_ptr()
+
+
+def _first(t: torch.Tensor, name: str):
+    """pointer to element 0 of a contiguous fp32 device tensor (a global scale, alone or as
+    element 0 of the quantizer's global-scale array)"""
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise TypeError(f"{name} must be a CUDA (ROCm) tensor")
+    if t.dtype != torch.float32 or t.numel() < 1 or not t.is_contiguous():
+        raise ValueError(f"{name} must be a contiguous float32 tensor with at least 1 element")
     return t.data_ptr()
 
 
@@ -316,7 +328,8 @@ def fgq_quantize_nvfp4(X: torch.Tensor, Xq: torch.Tensor | None = None,
                        scale_X: torch.Tensor | None = None,
                        global_scale: torch.Tensor | None = None, stream=None):
     """NVFP4 of bf16 X [R, C] (blocks of 16 along C): (packed codes uint8 [R, C/2], E4M3
-    block scales uint8 [R, C/16], fp32 global scale [1])."""
+    block scales uint8 [R, C/16], fp32 [FGQ_NVFP4_GLOBAL_FLOATS] whose element 0 is the global
+    scale and the rest scratch of the call)."""
     lib = load()
     R, C = X.shape
     dev = X.device
@@ -325,11 +338,12 @@ def fgq_quantize_nvfp4(X: torch.Tensor, Xq: torch.Tensor | None = None,
     if scale_X is None:
         scale_X = torch.empty((R, C // 16), dtype=torch.uint8, device=dev)
     if global_scale is None:
-        global_scale = torch.empty((1,), dtype=torch.float32, device=dev)
+        global_scale = torch.empty((FGQ_NVFP4_GLOBAL_FLOATS,), dtype=torch.float32, device=dev)
     _check("fgq_quantize_nvfp4", lib.fgq_quantize_nvfp4(
         _dev(X, "X", torch.bfloat16, (R, C)), _dev(Xq, "Xq", torch.uint8, (R, C // 2)),
         _dev(scale_X, "scale_X", torch.uint8, (R, C // 16)),
-        _dev(global_scale, "global_scale", torch.float32, (1,)), R, C, _stream(stream)))
+        _dev(global_scale, "global_scale", torch.float32, (FGQ_NVFP4_GLOBAL_FLOATS,)), R, C,
+        _stream(stream)))
     return Xq, scale_X, global_scale
 
 
@@ -352,9 +366,9 @@ def fgq_gemm_nvfp4(A_q: torch.Tensor, scale_A: torch.Tensor, global_A: torch.Ten
     _check("fgq_gemm_nvfp4", lib.fgq_gemm_nvfp4(
         _dev(A_q, "A_q", torch.uint8, (M, K // 2)),
         _dev(scale_A, "scale_A", torch.uint8, (M, K // 16)),
-        _dev(global_A, "global_A", torch.float32, (1,)),
+        _first(global_A, "global_A"),
         _dev(B_q, "B_q", torch.uint8, (N, K // 2)),
         _dev(scale_B, "scale_B", torch.uint8, (N, K // 16)),
-        _dev(global_B, "global_B", torch.float32, (1,)),
+        _first(global_B, "global_B"),
         _dev(C, "C", C.dtype, (M, N)), M, N, K, code, _stream(stream)))
     return C

@@ -13,6 +13,7 @@ using fgq_api::misaligned;
 using fgq_api::overlap;
 
 constexpr int64_t kMaxDim = (int64_t(1) << 31) - 1;
+static_assert(FGQ_NVFP4_GLOBAL_FLOATS == fgq::kNvfp4GlobalFloats, "NVFP4 global-scale array");
 
 // argument checks shared by the fp32-scale and UE8M0-scale entry points (ss: bytes per
 // scale); FGQ_OK for a valid call, including an empty one
@@ -325,7 +326,7 @@ int fgq_quantize_nvfp4(const void* X, void* Xq, uint8_t* scale_X, float* global_
     if (misaligned(X) || misaligned(Xq) || misaligned(scale_X) || misaligned(global_scale))
         return FGQ_ERR_ALIGN;
     const void* p[4] = {X, Xq, scale_X, global_scale};
-    const int64_t n[4] = {2 * R * C, R * C / 2, R * (C / 16), 4};
+    const int64_t n[4] = {2 * R * C, R * C / 2, R * (C / 16), 4 * FGQ_NVFP4_GLOBAL_FLOATS};
     for (int a = 0; a < 4; ++a)
         for (int b = a + 1; b < 4; ++b)
             if (overlap(p[a], n[a], p[b], n[b]))

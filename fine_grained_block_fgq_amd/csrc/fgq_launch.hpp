@@ -75,7 +75,9 @@ hipError_t launch_gemm_fp8_blockscaled_quant(const void* A_q, const float* sA, c
                                              hipStream_t stream);
 
 // NVFP4: quantize X [R,C] (blocks of 16 along C) to packed E2M1 codes [R,C/2], E4M3 block
-// scales [R,C/16] and the fp32 global scale *g; GEMM of A [M,K] and B stored [N,K]
+// scales [R,C/16] and the fp32 global scale g[0] (g: kNvfp4GlobalFloats floats, the rest
+// scratch of the call); GEMM of A [M,K] and B stored [N,K]
+constexpr int kNvfp4GlobalFloats = 512;
 hipError_t launch_quant_nvfp4(const void* X, void* Xq, uint8_t* sX, float* g, int64_t R,
                               int64_t C, hipStream_t stream);
 hipError_t launch_gemm_nvfp4(const void* A_q, const uint8_t* sA, const float* gA,

@@ -16,42 +16,46 @@ namespace fgq {
 
 // ---------------------------------------------------------------------------------------
 // Quantizer.  The global scale needs the tensor amax before any block can be coded, so a
-// call is three launches on one stream: clear the caller's global-scale output, reduce into
-// it (each workgroup's fl32(amax/2688) by an integer max of its bits, order-independent), then
-// code every block with the g it now holds.
+// call is two launches on one stream.  The caller's global-scale argument is an array of
+// kNvfp4GlobalFloats floats: the amax pass writes one candidate per workgroup into
+// g[2 .. 2+blocks) (fl32(amax_w/2688) of its share; a correctly rounded divide is monotonic,
+// so the largest candidate is the global scale of the tensor amax), with no atomics; every
+// wave of the coding pass reduces the candidates itself (non-negative fp32 values order like
+// their bit patterns), and the first workgroup writes g[0].  Nothing reads g[0] during the
+// call and nothing writes the candidates in the coding pass, so the two passes share the
+// array without a race.
 // ---------------------------------------------------------------------------------------
-__global__ void nvfp4_clear_kernel(uint32_t* slot)
-{
-    if (threadIdx.x == 0)
-        *slot = 0u;
-}
-
-// grid-stride max with four loads in flight per lane, reduced over the workgroup in LDS:
-// one atomic per workgroup.  The atomics on the one address are serialized (~10 ns each,
-// measured: 4096 workgroups cost 40 us more than 512), so the grid is capped at 256
-// workgroups, each lane taking at least 16 vectors.
+// up to 256 candidates, at g[4 .. 259] (16-byte aligned): every coding wave reads them with
+// one 16-byte load per lane and reduces them itself
 constexpr int NVFP4_AMAX_BLOCKS = 256;
+constexpr int NVFP4_CAND_OFF = 4;
+static_assert(NVFP4_CAND_OFF + NVFP4_AMAX_BLOCKS <= kNvfp4GlobalFloats, "candidate slots");
 constexpr int NVFP4_AMAX_VPT = 16;
-constexpr int NVFP4_AMAX_THREADS = 512;   // 8 waves: more loads in flight per CU than 4
+constexpr int NVFP4_AMAX_THREADS = 512;   // 8 waves (1024: 82 -> 85 us at 16384x7168)
 constexpr int NVFP4_AMAX_WAVES = NVFP4_AMAX_THREADS / 64;
 
+// grid-stride max with four loads in flight per lane, reduced over the workgroup in LDS,
+// written as this workgroup's candidate.  Ordinary (temporal) loads, so that X stays in the
+// Infinity Cache for the coding pass where it fits (4096x4096: 15.3 -> 14.6 us per call;
+// the coding pass's own loads, the last use of X, are non-temporal)
+#define AMAX_LOAD(p) (*(p))
 __global__ __launch_bounds__(NVFP4_AMAX_THREADS) void nvfp4_amax_kernel(
-    const u32x4* __restrict__ X, int64_t nvec, uint32_t* slot)
+    const u32x4* __restrict__ X, int64_t nvec, uint32_t* __restrict__ cand)
 {
     __shared__ uint32_t wave_amax[NVFP4_AMAX_WAVES];
     uint32_t m = 0;
     const int64_t stride = (int64_t)gridDim.x * NVFP4_AMAX_THREADS;
     int64_t i = (int64_t)blockIdx.x * NVFP4_AMAX_THREADS + threadIdx.x;
     for (; i + 3 * stride < nvec; i += 4 * stride) {
-        const u32x4 a = __builtin_nontemporal_load(&X[i]);
-        const u32x4 b = __builtin_nontemporal_load(&X[i + stride]);
-        const u32x4 c = __builtin_nontemporal_load(&X[i + 2 * stride]);
-        const u32x4 d = __builtin_nontemporal_load(&X[i + 3 * stride]);
+        const u32x4 a = AMAX_LOAD(&X[i]);
+        const u32x4 b = AMAX_LOAD(&X[i + stride]);
+        const u32x4 c = AMAX_LOAD(&X[i + 2 * stride]);
+        const u32x4 d = AMAX_LOAD(&X[i + 3 * stride]);
         m = max(max(m, max(absmax_bits8(a), absmax_bits8(b))),
                 max(absmax_bits8(c), absmax_bits8(d)));
     }
     for (; i < nvec; i += stride)
-        m = max(m, absmax_bits8(__builtin_nontemporal_load(&X[i])));
+        m = max(m, absmax_bits8(AMAX_LOAD(&X[i])));
     m = wave_max(m);
     if ((threadIdx.x & 63) == 0)
         wave_amax[threadIdx.x >> 6] = m;
@@ -61,10 +65,7 @@ __global__ __launch_bounds__(NVFP4_AMAX_THREADS) void nvfp4_amax_kernel(
 #pragma unroll
         for (int w = 0; w < NVFP4_AMAX_WAVES; ++w)
             b = max(b, wave_amax[w]);
-        // this workgroup's candidate global scale fl32(amax/2688): a correctly rounded divide
-        // is monotonic, so the largest candidate is the global scale of the tensor amax, and
-        // non-negative fp32 values order like their bit patterns
-        atomicMax(slot, __float_as_uint(__uint_as_float(b << 16) / 2688.0f));
+        cand[blockIdx.x] = __float_as_uint(__uint_as_float(b << 16) / 2688.0f);
     }
 }
 
@@ -83,60 +84,97 @@ __device__ __forceinline__ uint32_t e2m1_code(float y)
 // lane pair (2b, 2b+1), whose amax is exchanged by a DPP quad permute [1,0,3,2]
 constexpr int NVFP4_QV = 2;   // two vectors per lane: 7-9% faster than one, and than four
 
+// the 8 codes of one vector (packed nibbles) and its lane pair's E4M3 block scale
+__device__ __forceinline__ uint32_t nvfp4_code8(u32x4 v, float g, float six_g, uint32_t& sb_out)
+{
+    uint32_t am = absmax_bits8(v);
+    am = max(am, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)am, 0xB1, 0xF, 0xF, false));
+    uint32_t sb = 0;
+    if (six_g != 0.0f)
+        sb = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(__uint_as_float(am << 16) / six_g, 0.0f,
+                                                      0, false) &
+             0xFFu;
+    const float D = __builtin_amdgcn_cvt_f32_fp8((int)sb, 0) * g;
+    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+    uint32_t packed = 0;
+    if (D >= 0x1p-100f && D <= 0x1p100f) {
+        // y = fl32(x / D) without a divide per element: r = 1/D correctly rounded (one IEEE
+        // divide per lane), q = x*r, then Markstein's correction with the exact remainder
+        // x - q*D gives the correctly rounded quotient (Markstein's theorem: r within half an
+        // ulp of 1/D and q within one ulp of x/D; with the range guard, r and q stay normal
+        // and the remainder is exact wherever x/D is near an E2M1 rounding boundary, since
+        // the block scale keeps |x| < 9*D).  The E2M1 code is
+        // then the hardware convert at unit scale, which applies exactly the nearest-even,
+        // saturating rule (checked against it on every finite fp32 input).
+        const float r = 1.0f / D;
+        float y[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const uint32_t xb = (e & 1) ? (w[e >> 1] & 0xFFFF0000u) : (w[e >> 1] << 16);
+            const float x = __uint_as_float(xb);
+            const float q = x * r;
+            // negated remainder q*D - x, so that x = -0 keeps its sign: y = -0
+            y[e] = __builtin_fmaf(-__builtin_fmaf(q, D, -x), r, q);
+        }
+        packed = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(packed, y[0], y[1], 1.0f, 0);
+        packed = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(packed, y[2], y[3], 1.0f, 1);
+        packed = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(packed, y[4], y[5], 1.0f, 2);
+        packed = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(packed, y[6], y[7], 1.0f, 3);
+    } else {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const uint32_t b = (e & 1) ? (w[e >> 1] & 0xFFFF0000u) : (w[e >> 1] << 16);
+            const uint32_t c = D == 0.0f ? ((b >> 28) & 8u) : e2m1_code(__uint_as_float(b) / D);
+            packed |= c << (4 * e);
+        }
+    }
+    sb_out = sb;
+    return packed;
+}
+
+// the global scale: the largest of the amax pass's candidates (at most 256, four per lane),
+// for every wave by itself; the first workgroup's first lane writes it to gs[0]
+__device__ __forceinline__ float nvfp4_global(uint32_t* __restrict__ gs, int ncand)
+{
+    const int l = (int)(threadIdx.x & 63);
+    const uint32_t* cand = gs + NVFP4_CAND_OFF;
+    u32x4 c = u32x4{0u, 0u, 0u, 0u};
+    if (4 * l + 3 < ncand) {
+        c = *(const u32x4*)(cand + 4 * l);
+    } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+            if (4 * l + e < ncand)
+                c[e] = cand[4 * l + e];
+    }
+    const uint32_t gb = wave_max(max(max(c.x, c.y), max(c.z, c.w)));
+    if (blockIdx.x == 0 && threadIdx.x == 0)
+        gs[0] = gb;
+    return __uint_as_float(gb);
+}
+
+// coding pass: one workgroup per 256*NVFP4_QV vectors, the vectors requested before the global
+// scale is reduced
 __global__ __launch_bounds__(256) void nvfp4_quant_kernel(const u32x4* __restrict__ X,
                                                           uint32_t* __restrict__ Xq,
                                                           uint8_t* __restrict__ sX,
-                                                          const uint32_t* __restrict__ slot,
-                                                          int64_t nvec)
+                                                          uint32_t* __restrict__ gs,
+                                                          int ncand, int64_t nvec)
 {
-    const float g = __uint_as_float(*slot);
-    const float six_g = 6.0f * g;
-    // NVFP4_QV vectors per lane, 256 apart (lane pairs stay aligned to 16-element blocks)
+    const int64_t wg = blockIdx.x;
+    u32x4 v[NVFP4_QV];
 #pragma unroll
     for (int u = 0; u < NVFP4_QV; ++u) {
-        const int64_t i = (int64_t)blockIdx.x * (256 * NVFP4_QV) + u * 256 + threadIdx.x;
-        const u32x4 v = i < nvec ? __builtin_nontemporal_load(&X[i]) : u32x4{0u, 0u, 0u, 0u};
-        uint32_t am = absmax_bits8(v);
-        am = max(am, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)am, 0xB1, 0xF, 0xF, false));
-        uint32_t sb = 0;
-        if (six_g != 0.0f)
-            sb = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(__uint_as_float(am << 16) / six_g, 0.0f,
-                                                          0, false) &
-                 0xFFu;
-        const float D = __builtin_amdgcn_cvt_f32_fp8((int)sb, 0) * g;
-        const uint32_t w[4] = {v.x, v.y, v.z, v.w};
-        uint32_t packed = 0;
-        if (D >= 0x1p-100f && D <= 0x1p100f) {
-            // y = fl32(x / D) without a divide per element: r = 1/D correctly rounded (one IEEE
-            // divide per lane), q = x*r, then Markstein's correction with the exact remainder
-            // x - q*D gives the correctly rounded quotient (Markstein's theorem: r within half an
-            // ulp of 1/D and q within one ulp of x/D; with the range guard, r and q stay normal
-            // and the remainder is exact wherever x/D is near an E2M1 rounding boundary, since
-            // the block scale keeps |x| < 9*D).  The E2M1 code is
-            // then the hardware convert at unit scale, which applies exactly the nearest-even,
-            // saturating rule (checked against it on every finite fp32 input).
-            const float r = 1.0f / D;
-            float y[8];
+        const int64_t i = wg * (256 * NVFP4_QV) + u * 256 + threadIdx.x;
+        v[u] = i < nvec ? __builtin_nontemporal_load(&X[i]) : u32x4{0u, 0u, 0u, 0u};
+    }
+    const float g = nvfp4_global(gs, ncand);
+    const float six_g = 6.0f * g;
 #pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                const uint32_t xb = (e & 1) ? (w[e >> 1] & 0xFFFF0000u) : (w[e >> 1] << 16);
-                const float x = __uint_as_float(xb);
-                const float q = x * r;
-                // negated remainder q*D - x, so that x = -0 keeps its sign: y = -0
-                y[e] = __builtin_fmaf(-__builtin_fmaf(q, D, -x), r, q);
-            }
-            packed = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(packed, y[0], y[1], 1.0f, 0);
-            packed = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(packed, y[2], y[3], 1.0f, 1);
-            packed = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(packed, y[4], y[5], 1.0f, 2);
-            packed = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(packed, y[6], y[7], 1.0f, 3);
-        } else {
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                const uint32_t b = (e & 1) ? (w[e >> 1] & 0xFFFF0000u) : (w[e >> 1] << 16);
-                const uint32_t c = D == 0.0f ? ((b >> 28) & 8u) : e2m1_code(__uint_as_float(b) / D);
-                packed |= c << (4 * e);
-            }
-        }
+    for (int u = 0; u < NVFP4_QV; ++u) {
+        const int64_t i = wg * (256 * NVFP4_QV) + u * 256 + threadIdx.x;
+        uint32_t sb;
+        const uint32_t packed = nvfp4_code8(v[u], g, six_g, sb);
         if (i < nvec) {
             Xq[i] = packed;
             if ((threadIdx.x & 1) == 0)
@@ -148,22 +186,22 @@ __global__ __launch_bounds__(256) void nvfp4_quant_kernel(const u32x4* __restric
 hipError_t launch_quant_nvfp4(const void* X, void* Xq, uint8_t* sX, float* g, int64_t R,
                               int64_t C, hipStream_t stream)
 {
-    uint32_t* slot = reinterpret_cast<uint32_t*>(g);
+    uint32_t* const gs = reinterpret_cast<uint32_t*>(g);
     const int64_t nvec = R * C / 8;
     if (!grid_fits((nvec + 255) / 256, 256))
         return hipErrorInvalidConfiguration;
-    hipLaunchKernelGGL(nvfp4_clear_kernel, dim3(1), dim3(64), 0, stream, slot);
     int64_t ablocks = (nvec + NVFP4_AMAX_THREADS * NVFP4_AMAX_VPT - 1) /
                       (NVFP4_AMAX_THREADS * NVFP4_AMAX_VPT);
     ablocks = ablocks < 1 ? 1 : (ablocks > NVFP4_AMAX_BLOCKS ? NVFP4_AMAX_BLOCKS : ablocks);
     hipLaunchKernelGGL(nvfp4_amax_kernel, dim3((unsigned)ablocks), dim3(NVFP4_AMAX_THREADS), 0,
-                       stream,
-                       static_cast<const u32x4*>(X), nvec, slot);
-    hipLaunchKernelGGL(nvfp4_quant_kernel,
-                       dim3((unsigned)((nvec + 256 * NVFP4_QV - 1) / (256 * NVFP4_QV))), dim3(256),
-                       0,
-                       stream, static_cast<const u32x4*>(X), static_cast<uint32_t*>(Xq), sX,
-                       slot, nvec);
+                       stream, static_cast<const u32x4*>(X), nvec, gs + NVFP4_CAND_OFF);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess)
+        return e;
+    const int64_t qblocks = (nvec + 256 * NVFP4_QV - 1) / (256 * NVFP4_QV);
+    hipLaunchKernelGGL(nvfp4_quant_kernel, dim3((unsigned)qblocks), dim3(256), 0, stream,
+                       static_cast<const u32x4*>(X), static_cast<uint32_t*>(Xq), sX, gs,
+                       (int)ablocks, nvec);
     return hipGetLastError();
 }
 

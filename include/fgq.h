@@ -232,9 +232,12 @@ int fgq_gemm_fp8_blockscaled_ue8m0(const void* A_q, const uint8_t* scale_A, cons
  *   X            in : bf16 [R, C] row-major, C % 16 == 0, R*C <= 2^35
  *   Xq           out: packed codes [R, C/2], element 2i in the low nibble of byte i
  *   scale_X      out: E4M3 [R, C/16]
- *   global_scale out: one fp32 (also used as scratch by the call until it completes)
- * Three launches on `stream` (the tensor amax is needed before any block is coded).
+ *   global_scale out: fp32 [FGQ_NVFP4_GLOBAL_FLOATS]; element 0 receives the global scale, the
+ *                     others are scratch of the call (overwritten; the amax pass leaves one
+ *                     candidate per workgroup there, so no atomics and no clearing launch)
+ * Two launches on `stream` (the tensor amax is needed before any block is coded).
  */
+#define FGQ_NVFP4_GLOBAL_FLOATS 512
 int fgq_quantize_nvfp4(const void* X, void* Xq, uint8_t* scale_X, float* global_scale,
                        int64_t R, int64_t C, void* stream);
 /*

@@ -65,8 +65,9 @@ def test_quantizers_repeat(operands):
     repeat(lambda: fgq.fgq_quantize_weight_128x128_ue8m0(B, Bq, eB), [Bq, eB])
     q4 = torch.empty((M, K // 2), dtype=torch.uint8, device="cuda")
     s4 = torch.empty((M, K // 16), dtype=torch.uint8, device="cuda")
-    g4 = torch.empty((1,), dtype=torch.float32, device="cuda")
-    repeat(lambda: fgq.fgq_quantize_nvfp4(A, q4, s4, g4), [q4, s4, g4])
+    g4 = torch.empty((fgq.FGQ_NVFP4_GLOBAL_FLOATS,), dtype=torch.float32, device="cuda")
+    # element 0 of the global-scale array is the output; the rest is the call's scratch
+    repeat(lambda: fgq.fgq_quantize_nvfp4(A, q4, s4, g4), [q4, s4, g4[:1]])
 
 
 @pytest.mark.parametrize("variant", [0, 1, 2, 3, 4, 5])

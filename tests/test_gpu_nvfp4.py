@@ -19,7 +19,8 @@ def gpu_nvfp4(bits):
     R, C = bits.shape
     Xq = torch.full((R, C // 2), 0xEE, dtype=torch.uint8, device="cuda")
     sX = torch.full((R, C // 16), 0xFF, dtype=torch.uint8, device="cuda")
-    g = torch.full((1,), float("nan"), dtype=torch.float32, device="cuda")
+    g = torch.full((fgq.FGQ_NVFP4_GLOBAL_FLOATS,), float("nan"), dtype=torch.float32,
+                   device="cuda")
     fgq.fgq_quantize_nvfp4(dev_bf16(bits), Xq, sX, g)
     torch.cuda.synchronize()
     return Xq.cpu().numpy(), sX.cpu().numpy(), g.cpu().numpy()[0]
