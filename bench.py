@@ -86,7 +86,8 @@ def summarize(ktrace_dir, fetch_dir, write_dir, mfma_dir=None):
             return list(csv.DictReader(fh))
 
     def short(name):
-        for k in ("gemm_fp8_blockscaled_narrow_kernel", "gemm_fp8_blockscaled_kernel",
+        for k in ("gemm_fp8_blockscaled_narrow_kernel", "gemm_fp8_blockscaled_ksplit_kernel",
+                  "splitk_reduce_kernel", "gemm_fp8_blockscaled_kernel",
                   "gemm_nvfp4_kernel", "nvfp4_quant_kernel", "nvfp4_amax_kernel",
                   "quant_act_1x128_kernel", "quant_weight_128x128_kernel",
                   "vectorized_elementwise_kernel"):
@@ -150,9 +151,16 @@ def summarize(ktrace_dir, fetch_dir, write_dir, mfma_dir=None):
                                                      "bytes_per_launch": b}
     with open(os.path.join(PROFILES, "kernel_stats_bench_step.txt"), "w") as f:
         f.write("command: cd /tmp && export TMPDIR=/tmp; rocprofv3 --kernel-trace --stats -f csv "
-                "-d <dir> -o run -- python3 bench.py --no-cpu-baseline\n"
+                "-d <dir> -o run -- python3 bench.py --gpus 1 --steps 20 --warmup 5\n"
                 "summary: python3 bench.py --summarize <ktrace dir> <fetch dir> <write dir>\n\n")
         f.write(stats + "\n")
+        g = groups.get(("gemm_fp8_blockscaled_kernel", 262144))
+        if g:
+            avg = sum(g) / len(g) / 1e3
+            tf = 2.0 * 4096 ** 3 / (avg * 1e-6) / 1e12
+            f.write(f"\n4096^3 bf16 GEMM (grid 262144): {len(g)} launches, average {avg:.2f} us = "
+                    f"{tf:.1f} TFLOP/s = {tf / PEAK_FP8_TFLOPS:.4f} of the {PEAK_FP8_TFLOPS:.0f} "
+                    f"TFLOP/s dense FP8 peak ({tf / PEAK_F16_TFLOPS:.4f} of the f16 peak)\n")
     with open(os.path.join(PROFILES, "hbm_traffic_counters.txt"), "w") as f:
         f.write("commands: rocprofv3 --pmc FETCH_SIZE -f csv -d <dir> -o run -- python3 bench.py "
                 "--mode profile ; rocprofv3 --pmc WRITE_SIZE -f csv -d <dir> -o run -- python3 "
