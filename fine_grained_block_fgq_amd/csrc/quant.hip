@@ -73,21 +73,24 @@ __global__ __launch_bounds__(64 * ACT_WAVES) void quant_act_1x128_kernel(
 }
 
 // ---------------------------------------------------------------------------------------
-// 128x128 weight blocks.  One 256-thread workgroup per block: the block is 128 rows of 256
-// bytes = 2048 16-byte chunks, 8 per thread, all loaded before the reduction (32 KB in
-// flight per workgroup).  Chunk c = i*256 + tid covers row c/16, columns 8*(c%16)..+7, so
+// 128x128 weight blocks.  One 512-thread workgroup per block: the block is 128 rows of 256
+// bytes = 2048 16-byte chunks, 4 per thread, all loaded before the reduction (32 KB in
+// flight per workgroup).  Chunk c = i*512 + tid covers row c/16, columns 8*(c%16)..+7, so
 // each load instruction of a wave reads 4 whole 256-byte row segments.  amax: per-thread
-// max, DPP + readlane across the wave, LDS across the 4 waves.
+// max, DPP + readlane across the wave, LDS across the 8 waves.  (Timed on [16384,7168]:
+// 128/256/512/1024 threads 65.3/61.9/60.8/62.5 us per launch; ordinary loads instead of
+// non-temporal ones 66.4, workgroups ordered down the K blocks first 69.2.)
 // ---------------------------------------------------------------------------------------
-constexpr int WQ_THREADS = 256;
+constexpr int WQ_THREADS = 512;
 constexpr int WQ_CHUNKS = 2048 / WQ_THREADS;
+constexpr int WQ_WAVES = WQ_THREADS / 64;
 
 template <class Scale>
 __global__ __launch_bounds__(WQ_THREADS) void quant_weight_128x128_kernel(
     const uint8_t* __restrict__ W, uint8_t* __restrict__ Wq,
     typename Scale::stored_t* __restrict__ sW, int64_t N)
 {
-    __shared__ uint32_t wave_amax[WQ_THREADS / 64];
+    __shared__ uint32_t wave_amax[WQ_WAVES];
     const int tid = threadIdx.x;
     const int64_t nb = blockIdx.x, kb = blockIdx.y;
     const int64_t NB = N / 128;
@@ -110,7 +113,10 @@ __global__ __launch_bounds__(WQ_THREADS) void quant_weight_128x128_kernel(
     if ((tid & 63) == 0)
         wave_amax[tid >> 6] = m;
     __syncthreads();
-    m = max(max(wave_amax[0], wave_amax[1]), max(wave_amax[2], wave_amax[3]));
+    m = wave_amax[0];
+#pragma unroll
+    for (int w = 1; w < WQ_WAVES; ++w)
+        m = max(m, wave_amax[w]);
     const Scale g(m);
 #pragma unroll
     for (int i = 0; i < WQ_CHUNKS; ++i) {
