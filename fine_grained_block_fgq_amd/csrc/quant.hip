@@ -77,9 +77,10 @@ __global__ __launch_bounds__(64 * ACT_WAVES) void quant_act_1x128_kernel(
 // bytes = 2048 16-byte chunks, 4 per thread, all loaded before the reduction (32 KB in
 // flight per workgroup).  Chunk c = i*512 + tid covers row c/16, columns 8*(c%16)..+7, so
 // each load instruction of a wave reads 4 whole 256-byte row segments.  amax: per-thread
-// max, DPP + readlane across the wave, LDS across the 8 waves.  (Timed on [16384,7168]:
-// 128/256/512/1024 threads 65.3/61.9/60.8/62.5 us per launch; ordinary loads instead of
-// non-temporal ones 66.4, workgroups ordered down the K blocks first 69.2.)
+// max, DPP + readlane across the wave, LDS across the 8 waves.  Loads are non-temporal, the
+// code stores ordinary.  (Timed on [16384,7168]: 128/256/512/1024 threads 65.3/61.9/60.8/62.5
+// us per launch with non-temporal stores, 57.3 us with ordinary stores; ordinary loads 66.4,
+// workgroups ordered down the K blocks first 69.2.)
 // ---------------------------------------------------------------------------------------
 constexpr int WQ_THREADS = 512;
 constexpr int WQ_CHUNKS = 2048 / WQ_THREADS;
@@ -122,8 +123,10 @@ __global__ __launch_bounds__(WQ_THREADS) void quant_weight_128x128_kernel(
     for (int i = 0; i < WQ_CHUNKS; ++i) {
         const int c = i * WQ_THREADS + tid;
         const int row = c >> 4, col8 = (c & 15) * 8;
-        __builtin_nontemporal_store(g.quant(v[i]),
-                                    reinterpret_cast<u32x2*>(qblk + (int64_t)row * N + col8));
+        // ordinary stores, measured faster than non-temporal ones here (likely because a row's
+        // 128-byte code segment is combined in L2 with the adjacent column blocks' segments
+        // before it is written to HBM)
+        *reinterpret_cast<u32x2*>(qblk + (int64_t)row * N + col8) = g.quant(v[i]);
     }
     if (tid == 0)
         sW[kb * NB + nb] = g.stored();
